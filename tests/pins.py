@@ -1,0 +1,165 @@
+"""Checks that pin the oracle to what the pages and the mathematics fix.
+
+Each check takes the implementation under test as an argument, so the same
+check runs on the oracle (tests/test_oracle_*.py) and on deliberately broken
+copies of it (tests/test_oracle_mutations.py), which it must reject.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import synth
+
+
+def sdpa64(q, k, v, scale, causal=False):
+    """torch's CPU scaled_dot_product_attention in float64.
+    q: [..., Lq, d]; k, v: [..., Lk, d]."""
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64)) for x in (q, k, v))
+    return F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale).numpy()
+
+
+# ---------------------------------------------------------------------------
+# temporal attention
+# ---------------------------------------------------------------------------
+def check_temporal_closed_form(temporal_impl, p_max=9, n=4, writes=(1, 4, 4, 4), S=3, H=2):
+    """K == 0 makes every visible logit equal, so output i is the mean of the
+    visible values. With one-hot frame codes as values the output spells out
+    exactly which frames query i sees and how many. Checked after each write,
+    so both the growing queue and the post-eviction (wrapped ring) states are
+    covered. Returns the max error."""
+    from oracle import TemporalQueue
+    d = p_max + n            # one code dimension per logical key position
+    B = 1
+    q_ = TemporalQueue(p_max)
+    ring_k = np.zeros((B, p_max, S, H, d))
+    ring_v = np.zeros((B, p_max, S, H, d))
+    frame = 0
+    worst = 0.0
+    for w in writes:
+        # state before this write: P_k cached frames, logical j -> slot
+        slots = q_.slot_map()
+        P_k = len(slots)
+        # values of the cached frame at logical j: one-hot e_j; new frame i: e_{P_k+i}
+        for j, s in enumerate(slots):
+            ring_v[:, s] = 0.0
+            ring_v[:, s, :, :, j] = 1.0
+        k_new = np.zeros((B, n, S, H, d))
+        v_new = np.zeros((B, n, S, H, d))
+        for i in range(n):
+            v_new[:, i, :, :, P_k + i] = 1.0
+        q = np.random.default_rng(frame).standard_normal((B, n, S, H, d))
+        out = temporal_impl(q, k_new, v_new, ring_k, ring_v, slots, 0.37)
+        for i in range(n):
+            expect = np.zeros(d)
+            expect[:P_k + i + 1] = 1.0 / (P_k + i + 1)
+            worst = max(worst, float(np.max(np.abs(out[:, i] - expect))))
+        # write w frames (their values are rewritten before the next call)
+        q_.write(range(frame, frame + w))
+        frame += w
+    return worst
+
+
+def check_temporal_vs_recompute(temporal_impl, shape, seed=3, writes=(1, 4, 4, 4, 4)):
+    """Cached-prefix attention equals brute-force masked attention over the
+    whole frame sequence, before and after eviction. Returns max abs error."""
+    from oracle import TemporalQueue, full_recompute_temporal_ref
+    B, S, H, d, n, p_max = (shape[k] for k in ("B", "S", "H", "d", "l", "p_max"))
+    scale = 1.0 / np.sqrt(d)
+    queue = TemporalQueue(p_max)
+    ring_k = np.zeros((B, p_max, S, H, d))
+    ring_v = np.zeros((B, p_max, S, H, d))
+    frame = 0
+    worst = 0.0
+    for step, w in enumerate(writes):
+        if frame > 0:
+            q = synth.step_tensor(seed, "q", step, 1, B, n, S, H, d)
+            k = synth.step_tensor(seed, "k", step, 1, B, n, S, H, d)
+            v = synth.step_tensor(seed, "v", step, 1, B, n, S, H, d)
+            got = temporal_impl(q, k, v, ring_k, ring_v, queue.slot_map(), scale)
+            kseq = np.concatenate([synth.frames_tensor(seed, "kt", range(frame), B, S, H, d), k], 1)
+            vseq = np.concatenate([synth.frames_tensor(seed, "vt", range(frame), B, S, H, d), v], 1)
+            ref = full_recompute_temporal_ref(q, kseq, vseq, frame, p_max, scale)
+            worst = max(worst, float(np.max(np.abs(got - ref))))
+        frames = list(range(frame, frame + w))
+        slots = queue.write(frames)
+        kt = synth.frames_tensor(seed, "kt", frames, B, S, H, d)
+        vt = synth.frames_tensor(seed, "vt", frames, B, S, H, d)
+        for i, s in enumerate(slots):
+            ring_k[:, s] = kt[:, i]
+            ring_v[:, s] = vt[:, i]
+        frame += w
+    return worst
+
+
+def check_temporal_empty_queue_is_causal_sdpa(temporal_impl, B=2, n=5, S=3, H=2, d=8, seed=1):
+    """P_k = 0: causal attention over the n new frames, i.e. torch's causal SDPA."""
+    g = np.random.default_rng(seed)
+    q, k, v = (g.standard_normal((B, n, S, H, d)) for _ in range(3))
+    scale = 0.29
+    got = temporal_impl(q, k, v, np.zeros((B, 1, S, H, d)), np.zeros((B, 1, S, H, d)), [], scale)
+    # rows (b, s, h) -> SDPA batch; frames -> sequence
+    perm = (0, 2, 3, 1, 4)
+    ref = sdpa64(q.transpose(perm), k.transpose(perm), v.transpose(perm), scale, causal=True)
+    return float(np.max(np.abs(got.transpose(perm) - ref)))
+
+
+def check_temporal_single_query_is_sdpa(temporal_impl, B=1, p_max=6, S=4, H=3, d=8, seed=2):
+    """n = 1: the query sees every cached frame and itself, no mask -> SDPA."""
+    g = np.random.default_rng(seed)
+    ring_k = g.standard_normal((B, p_max, S, H, d))
+    ring_v = g.standard_normal((B, p_max, S, H, d))
+    q, k, v = (g.standard_normal((B, 1, S, H, d)) for _ in range(3))
+    slots = [4, 5, 0, 1]                     # a wrapped queue of 4 frames
+    scale = 0.41
+    got = temporal_impl(q, k, v, ring_k, ring_v, slots, scale)
+    keys = np.concatenate([ring_k[:, slots], k], 1)
+    vals = np.concatenate([ring_v[:, slots], v], 1)
+    perm = (0, 2, 3, 1, 4)
+    ref = sdpa64(q.transpose(perm), keys.transpose(perm), vals.transpose(perm), scale)
+    return float(np.max(np.abs(got.transpose(perm) - ref)))
+
+
+# ---------------------------------------------------------------------------
+# spatial attention
+# ---------------------------------------------------------------------------
+def check_spatial_vs_sdpa(spatial_impl, B=2, n=3, S=5, H=2, d=8, p=2, seed=4):
+    """Prefix mode equals SDPA over the token-axis concatenation [own frame,
+    prefix frames in logical order]; self mode and P' = 0 equal SDPA over the
+    own frame. Returns the max error over the three cases."""
+    g = np.random.default_rng(seed)
+    q, k, v = (g.standard_normal((B, n, S, H, d)) for _ in range(3))
+    ks, vs = (g.standard_normal((B, p + 1, S, H, d)) for _ in range(2))
+    slots = [2, 0]                       # logical order != physical order
+    scale = 0.33
+    worst = 0.0
+    got = spatial_impl(q, k, v, ks, vs, slots, scale, "prefix")
+    for f in range(n):
+        kk = np.concatenate([k[:, f]] + [ks[:, s] for s in slots], 1)   # [B][Sk][H][d]
+        vv = np.concatenate([v[:, f]] + [vs[:, s] for s in slots], 1)
+        ref = sdpa64(q[:, f].transpose(0, 2, 1, 3), kk.transpose(0, 2, 1, 3),
+                     vv.transpose(0, 2, 1, 3), scale)
+        worst = max(worst, float(np.max(np.abs(got[:, f].transpose(0, 2, 1, 3) - ref))))
+    for mode, sl in (("self", slots), ("prefix", [])):
+        got = spatial_impl(q, k, v, ks, vs, sl, scale, mode)
+        for f in range(n):
+            ref = sdpa64(q[:, f].transpose(0, 2, 1, 3), k[:, f].transpose(0, 2, 1, 3),
+                         v[:, f].transpose(0, 2, 1, 3), scale)
+            worst = max(worst, float(np.max(np.abs(got[:, f].transpose(0, 2, 1, 3) - ref))))
+    return worst
+
+
+def check_spatial_zero_query(spatial_impl, B=1, n=2, S=6, H=2, d=4, p=3, seed=5):
+    """Q == 0: uniform weights, output = mean of all (P'+1)*S value rows."""
+    g = np.random.default_rng(seed)
+    q = np.zeros((B, n, S, H, d))
+    k, v = (g.standard_normal((B, n, S, H, d)) for _ in range(2))
+    ks, vs = (g.standard_normal((B, p, S, H, d)) for _ in range(2))
+    slots = list(range(p))
+    got = spatial_impl(q, k, v, ks, vs, slots, 1.0, "prefix")
+    worst = 0.0
+    for f in range(n):
+        mean = (v[:, f].sum(1) + vs.sum((1, 2))) / ((p + 1) * S)          # [B][H][d]
+        worst = max(worst, float(np.max(np.abs(got[:, f] - mean[:, None]))))
+    return worst
