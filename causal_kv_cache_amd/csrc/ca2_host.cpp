@@ -1,0 +1,374 @@
+// Host side of libca2: cache object, validation, queue / spatial-buffer / TPE
+// bookkeeping and kernel launches behind the C ABI declared in include/ca2.h.
+//
+// The whole queue state is one counter, frames_written (F_w). Clean frame F
+// lives in ring slot F mod P_max; the queue holds the last
+// P_k = min(F_w, P_max) frames, the oldest in slot (F_w - P_k) mod P_max
+// (Ca2-VDM notes, key design 4: FIFO queue capped at P_max, oldest leaves
+// first). The spatial buffer keeps the last P' clean frames, frame F in slot
+// F mod P' (key design 5); while fewer than P' exist, the oldest fills the
+// missing logical positions. TPE index of frame F is F mod L_tpe (key design
+// 4, Cyclic-TPEs).
+#include "ca2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "kernels.hpp"
+
+struct ca2_cache {
+  ca2_config cfg;
+  int64_t frames_written;
+  int64_t frame_bytes;   // S * H * d * elem: one (batch entry, frame) block
+  void* ring_k;
+  void* ring_v;
+  void* sp_k;
+  void* sp_v;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ca2_status fail(ca2_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+ca2_status ok() {
+  g_last_error.clear();
+  return CA2_OK;
+}
+
+int elem_bytes(int dtype) { return dtype == CA2_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+ca2_status check_config(const ca2_config* c) {
+  if (!c) return fail(CA2_ERR_INVALID_ARG, "config is NULL");
+  if (c->dtype != CA2_F32 && c->dtype != CA2_BF16) return fail(CA2_ERR_INVALID_ARG, "dtype %d", c->dtype);
+  if (c->batch < 1 || c->heads < 1 || c->tokens < 1 || c->head_dim < 1)
+    return fail(CA2_ERR_INVALID_ARG, "batch/heads/tokens/head_dim must be >= 1");
+  if (c->chunk < 1 || c->chunk > 16) return fail(CA2_ERR_INVALID_ARG, "chunk %d not in [1, 16]", c->chunk);
+  if (c->p_max < 1) return fail(CA2_ERR_INVALID_ARG, "p_max %d < 1", c->p_max);
+  if (c->p_spatial < 0 || c->p_spatial >= c->chunk)
+    return fail(CA2_ERR_INVALID_ARG, "p_spatial %d must satisfy 0 <= P' < chunk (%d)", c->p_spatial, c->chunk);
+  if ((int64_t)c->tpe_len < (int64_t)c->p_max + c->chunk)
+    return fail(CA2_ERR_INVALID_ARG, "tpe_len %d < p_max + chunk", c->tpe_len);
+  const int64_t rows = (int64_t)c->batch * c->tokens * c->heads;
+  if (rows > (int64_t)1 << 30) return fail(CA2_ERR_INVALID_ARG, "B*S*H too large");
+  const int64_t frame = (int64_t)c->tokens * c->heads * c->head_dim * elem_bytes(c->dtype);
+  if ((int64_t)c->batch * (c->p_max + c->p_spatial) * frame > ((int64_t)1 << 46))
+    return fail(CA2_ERR_INVALID_ARG, "cache too large");
+  if (!ca2::temporal_supported(c->dtype, c->head_dim) || !ca2::spatial_supported(c->dtype, c->head_dim))
+    return fail(CA2_ERR_UNSUPPORTED, "head_dim %d not built for dtype %d", c->head_dim, c->dtype);
+  return CA2_OK;
+}
+
+ca2_status check_frames(const ca2_cache* c, int32_t n) {
+  if (!c) return fail(CA2_ERR_INVALID_ARG, "cache is NULL");
+  if (n < 1 || n > c->cfg.chunk) return fail(CA2_ERR_INVALID_ARG, "n_frames %d not in [1, %d]", n, c->cfg.chunk);
+  return CA2_OK;
+}
+
+ca2_status check_ptrs(std::initializer_list<const void*> ps) {
+  int i = 0;
+  for (const void* p : ps) {
+    if (!p) return fail(CA2_ERR_INVALID_ARG, "device pointer argument %d is NULL", i);
+    if (!aligned16(p)) return fail(CA2_ERR_INVALID_ARG, "device pointer argument %d is not 16-byte aligned", i);
+    ++i;
+  }
+  return CA2_OK;
+}
+
+ca2_status hip_fail(hipError_t e, const char* what) {
+  return fail(CA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int32_t queue_len(const ca2_cache* c) {
+  return (int32_t)(c->frames_written < c->cfg.p_max ? c->frames_written : c->cfg.p_max);
+}
+
+int32_t queue_head(const ca2_cache* c) {
+  return (int32_t)((c->frames_written - queue_len(c)) % c->cfg.p_max);
+}
+
+// Logical spatial position j -> absolute frame (oldest first, padded by the
+// oldest while fewer than P' clean frames exist).
+int64_t spatial_frame(int64_t fw, int32_t p, int32_t j) {
+  const int64_t f = fw - p + j;
+  return f < 0 ? 0 : f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ca2_status_string(ca2_status s) {
+  switch (s) {
+    case CA2_OK: return "ok";
+    case CA2_ERR_INVALID_ARG: return "invalid argument";
+    case CA2_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case CA2_ERR_HIP: return "HIP runtime error";
+    case CA2_ERR_STATE: return "invalid in the cache's current state";
+    case CA2_ERR_UNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+const char* ca2_last_error(void) { return g_last_error.c_str(); }
+
+uint64_t ca2_bytes_resident(const ca2_config* cfg) {
+  if (check_config(cfg) != CA2_OK) return 0;
+  const uint64_t frame = (uint64_t)cfg->tokens * cfg->heads * cfg->head_dim * elem_bytes(cfg->dtype);
+  return 2ull * cfg->batch * (uint64_t)(cfg->p_max + cfg->p_spatial) * frame;
+}
+
+ca2_status ca2_cache_create(const ca2_config* cfg, ca2_cache** out) {
+  if (!out) return fail(CA2_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  ca2_status st = check_config(cfg);
+  if (st != CA2_OK) return st;
+  ca2_cache* c = new (std::nothrow) ca2_cache();
+  if (!c) return fail(CA2_ERR_OUT_OF_MEMORY, "host allocation failed");
+  c->cfg = *cfg;
+  c->frames_written = 0;
+  c->frame_bytes = (int64_t)cfg->tokens * cfg->heads * cfg->head_dim * elem_bytes(cfg->dtype);
+  const size_t ring_bytes = (size_t)cfg->batch * cfg->p_max * c->frame_bytes;
+  const size_t sp_bytes = (size_t)cfg->batch * cfg->p_spatial * c->frame_bytes;
+  // Unwritten slots are filled with 0xFF bytes (a NaN in both dtypes) when
+  // CA2_NAN_CANARY=1, so a kernel reading a slot it should not shows up as NaN.
+  const char* canary = getenv("CA2_NAN_CANARY");
+  const int fill = (canary && canary[0] == '1') ? 0xFF : 0x00;
+  void** bufs[4] = {&c->ring_k, &c->ring_v, &c->sp_k, &c->sp_v};
+  const size_t sizes[4] = {ring_bytes, ring_bytes, sp_bytes, sp_bytes};
+  for (int i = 0; i < 4; ++i) {
+    *bufs[i] = nullptr;
+    if (!sizes[i]) continue;
+    hipError_t e = hipMalloc(bufs[i], sizes[i]);
+    if (e != hipSuccess) {
+      ca2_cache_destroy(c);
+      (void)hipGetLastError();
+      return e == hipErrorOutOfMemory ? fail(CA2_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) failed", sizes[i])
+                                      : hip_fail(e, "hipMalloc");
+    }
+    e = hipMemset(*bufs[i], fill, sizes[i]);
+    if (e != hipSuccess) {
+      ca2_cache_destroy(c);
+      return hip_fail(e, "hipMemset");
+    }
+  }
+  *out = c;
+  return ok();
+}
+
+void ca2_cache_destroy(ca2_cache* c) {
+  if (!c) return;
+  if (c->ring_k) (void)hipFree(c->ring_k);
+  if (c->ring_v) (void)hipFree(c->ring_v);
+  if (c->sp_k) (void)hipFree(c->sp_k);
+  if (c->sp_v) (void)hipFree(c->sp_v);
+  delete c;
+}
+
+ca2_status ca2_cache_write(ca2_cache* c, const void* k_t, const void* v_t, const void* k_s,
+                           const void* v_s, int32_t n, void* stream) {
+  ca2_status st = check_frames(c, n);
+  if (st != CA2_OK) return st;
+  st = check_ptrs({k_t, v_t});
+  if (st != CA2_OK) return st;
+  const int32_t P = c->cfg.p_max, Ps = c->cfg.p_spatial;
+  if (Ps > 0) {
+    st = check_ptrs({k_s, v_s});
+    if (st != CA2_OK) return st;
+  }
+  ca2::CopyArgs a;
+  memset(&a, 0, sizeof(a));
+  a.batch = c->cfg.batch;
+  a.frame_bytes = c->frame_bytes;
+  const int64_t fw = c->frames_written;
+  const int64_t fb = c->frame_bytes;
+  int nj = 0;
+  // temporal ring: frame fw+i -> slot (fw+i) mod P; only the last P survive
+  for (int32_t i = (n > P ? n - P : 0); i < n; ++i) {
+    const int64_t slot = (fw + i) % P;
+    const void* srcs[2] = {k_t, v_t};
+    void* dsts[2] = {c->ring_k, c->ring_v};
+    for (int t = 0; t < 2; ++t) {
+      a.job[nj].src = static_cast<const unsigned char*>(srcs[t]) + i * fb;
+      a.job[nj].dst = static_cast<unsigned char*>(dsts[t]) + slot * fb;
+      a.job[nj].src_bstride = (int64_t)n * fb;
+      a.job[nj].dst_bstride = (int64_t)P * fb;
+      ++nj;
+    }
+  }
+  // spatial buffer: last P' frames, frame F -> slot F mod P'
+  for (int32_t i = (n > Ps ? n - Ps : 0); Ps > 0 && i < n; ++i) {
+    const int64_t slot = (fw + i) % Ps;
+    const void* srcs[2] = {k_s, v_s};
+    void* dsts[2] = {c->sp_k, c->sp_v};
+    for (int t = 0; t < 2; ++t) {
+      a.job[nj].src = static_cast<const unsigned char*>(srcs[t]) + i * fb;
+      a.job[nj].dst = static_cast<unsigned char*>(dsts[t]) + slot * fb;
+      a.job[nj].src_bstride = (int64_t)n * fb;
+      a.job[nj].dst_bstride = (int64_t)Ps * fb;
+      ++nj;
+    }
+  }
+  a.n_jobs = nj;
+  hipError_t e = ca2::launch_copy(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cache_write launch");
+  c->frames_written += n;
+  return ok();
+}
+
+ca2_status ca2_temporal_attn(const ca2_cache* c, const void* q, const void* k_new, const void* v_new,
+                             void* out, int32_t n, float scale, void* stream) {
+  ca2_status st = check_frames(c, n);
+  if (st != CA2_OK) return st;
+  st = check_ptrs({q, k_new, v_new, out});
+  if (st != CA2_OK) return st;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(CA2_ERR_INVALID_ARG, "scale must be finite and > 0");
+  ca2::TemporalArgs a;
+  a.q = q; a.k_new = k_new; a.v_new = v_new; a.out = out;
+  a.ring_k = c->ring_k; a.ring_v = c->ring_v;
+  a.rows_per_batch = c->cfg.tokens * c->cfg.heads;
+  a.rows_total = c->cfg.batch * a.rows_per_batch;
+  a.n = n;
+  a.p_k = queue_len(c);
+  a.head = queue_head(c);
+  a.p_max = c->cfg.p_max;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  hipError_t e = ca2::launch_temporal(c->cfg.dtype, c->cfg.head_dim, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "temporal_attn launch");
+  return ok();
+}
+
+ca2_status ca2_spatial_attn(const ca2_cache* c, const void* q, const void* k, const void* v, void* out,
+                            int32_t n, int32_t mode, float scale, void* stream) {
+  ca2_status st = check_frames(c, n);
+  if (st != CA2_OK) return st;
+  st = check_ptrs({q, k, v, out});
+  if (st != CA2_OK) return st;
+  if (mode != CA2_SPATIAL_PREFIX && mode != CA2_SPATIAL_SELF) return fail(CA2_ERR_INVALID_ARG, "mode %d", mode);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(CA2_ERR_INVALID_ARG, "scale must be finite and > 0");
+  const int32_t Ps = c->cfg.p_spatial;
+  ca2::SpatialArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.sp_k = c->sp_k; a.sp_v = c->sp_v;
+  a.batch = c->cfg.batch; a.n = n; a.tokens = c->cfg.tokens; a.heads = c->cfg.heads;
+  a.p_slots = Ps;
+  a.n_prefix = 0;
+  if (mode == CA2_SPATIAL_PREFIX && Ps > 0) {
+    if (c->frames_written < 1)
+      return fail(CA2_ERR_STATE, "prefix mode needs at least one clean frame in the cache");
+    a.n_prefix = Ps;
+    for (int32_t j = 0; j < Ps; ++j) a.prefix_slot[j] = (int32_t)(spatial_frame(c->frames_written, Ps, j) % Ps);
+  }
+  a.scale_log2e = scale * 1.4426950408889634f;
+  hipError_t e = ca2::launch_spatial(c->cfg.dtype, c->cfg.head_dim, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "spatial_attn launch");
+  return ok();
+}
+
+ca2_status ca2_tpe_index_raw(int64_t first, int32_t n, int32_t L, int32_t* out) {
+  if (first < 0 || n < 0 || L < 1) return fail(CA2_ERR_INVALID_ARG, "first >= 0, n >= 0, tpe_len >= 1");
+  if (n > 0 && !out) return fail(CA2_ERR_INVALID_ARG, "host_out is NULL");
+  for (int32_t i = 0; i < n; ++i) out[i] = (int32_t)((first + i) % L);
+  return ok();
+}
+
+ca2_status ca2_tpe_index(const ca2_cache* c, int32_t n, int32_t* out) {
+  ca2_status st = check_frames(c, n);
+  if (st != CA2_OK) return st;
+  return ca2_tpe_index_raw(c->frames_written, n, c->cfg.tpe_len, out);
+}
+
+ca2_status ca2_cache_info_get(const ca2_cache* c, ca2_cache_info* out) {
+  if (!c || !out) return fail(CA2_ERR_INVALID_ARG, "NULL argument");
+  out->p_k = queue_len(c);
+  out->head_slot = queue_head(c);
+  const int64_t fw = c->frames_written;
+  out->spatial_frames = (int32_t)(fw < c->cfg.p_spatial ? fw : c->cfg.p_spatial);
+  out->reserved = 0;
+  out->frames_written = fw;
+  out->bytes_resident = ca2_bytes_resident(&c->cfg);
+  return ok();
+}
+
+ca2_status ca2_ring_slot_map_raw(int64_t fw, int32_t P, int32_t* out, int32_t* p_k_out) {
+  if (fw < 0 || P < 1) return fail(CA2_ERR_INVALID_ARG, "frames_written >= 0, p_max >= 1");
+  const int32_t pk = (int32_t)(fw < P ? fw : P);
+  if (pk > 0 && !out) return fail(CA2_ERR_INVALID_ARG, "host_out is NULL");
+  for (int32_t j = 0; j < pk; ++j) out[j] = (int32_t)((fw - pk + j) % P);
+  if (p_k_out) *p_k_out = pk;
+  return ok();
+}
+
+ca2_status ca2_spatial_slot_map_raw(int64_t fw, int32_t Ps, int64_t* frames_out, int32_t* slots_out) {
+  if (fw < 0 || Ps < 0) return fail(CA2_ERR_INVALID_ARG, "frames_written >= 0, p_spatial >= 0");
+  if (fw == 0 || Ps == 0) return ok();
+  for (int32_t j = 0; j < Ps; ++j) {
+    const int64_t f = spatial_frame(fw, Ps, j);
+    if (frames_out) frames_out[j] = f;
+    if (slots_out) slots_out[j] = (int32_t)(f % Ps);
+  }
+  return ok();
+}
+
+ca2_status ca2_cache_slot_map(const ca2_cache* c, int32_t* out) {
+  if (!c) return fail(CA2_ERR_INVALID_ARG, "cache is NULL");
+  return ca2_ring_slot_map_raw(c->frames_written, c->cfg.p_max, out, nullptr);
+}
+
+ca2_status ca2_cache_frame_ids(const ca2_cache* c, int64_t* t_out, int64_t* s_out, int32_t* s_slots) {
+  if (!c) return fail(CA2_ERR_INVALID_ARG, "cache is NULL");
+  const int32_t pk = queue_len(c);
+  if (t_out)
+    for (int32_t j = 0; j < pk; ++j) t_out[j] = c->frames_written - pk + j;
+  return ca2_spatial_slot_map_raw(c->frames_written, c->cfg.p_spatial, s_out, s_slots);
+}
+
+ca2_status ca2_cache_debug_copy(const ca2_cache* c, void* hk, void* hv, void* hks, void* hvs, void* stream) {
+  if (!c) return fail(CA2_ERR_INVALID_ARG, "cache is NULL");
+  const size_t ring = (size_t)c->cfg.batch * c->cfg.p_max * c->frame_bytes;
+  const size_t sp = (size_t)c->cfg.batch * c->cfg.p_spatial * c->frame_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  struct { void* dst; const void* src; size_t n; } cp[4] = {
+      {hk, c->ring_k, ring}, {hv, c->ring_v, ring}, {hks, c->sp_k, sp}, {hvs, c->sp_v, sp}};
+  for (auto& x : cp) {
+    if (!x.dst || !x.n) continue;
+    hipError_t e = hipMemcpyAsync(x.dst, x.src, x.n, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  }
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  return ok();
+}
+
+ca2_status ca2_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int32_t m, int32_t c_in,
+                        int32_t c_out, void* stream) {
+  ca2_status st = check_ptrs({x, w, q, k, v});
+  if (st != CA2_OK) return st;
+  if (m < 1 || c_in < 64 || c_out < 64 || c_in % 64 || c_out % 64)
+    return fail(CA2_ERR_INVALID_ARG, "m >= 1, c_in and c_out multiples of 64");
+  if ((int64_t)m * c_in > ((int64_t)1 << 40)) return fail(CA2_ERR_INVALID_ARG, "too large");
+  ca2::ProjArgs a{x, w, q, k, v, m, c_in, c_out};
+  hipError_t e = ca2::launch_qkv_proj(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "qkv_proj launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Cache write: bitwise copy of clean frames into the temporal ring and the
+// spatial buffer (Ca2-VDM notes, overall framework -- the cache-writing stage
+// stores the clean chunk's K/V; key design 4 -- FIFO queue; key design 5 --
+// spatial buffer overwritten each step). One launch copies every
+// (tensor, frame) job for every batch entry; a (b, frame) block is one
+// contiguous run of S*H*d elements in both source and destination, so the
+// copy is a straight stream of 16-byte loads and stores.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace ca2 {
+namespace {
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_frames_kernel(CopyArgs a) {
+  // Read the job through the kernel-argument segment (uniform scalar loads);
+  // indexing the by-value struct with blockIdx.y would copy it to LDS.
+  const CopyArgs* args = reinterpret_cast<const CopyArgs*>(__builtin_amdgcn_kernarg_segment_ptr());
+  const CopyJob j = args->job[blockIdx.y];
+  const int b = blockIdx.z;
+  const uint4* __restrict__ src = reinterpret_cast<const uint4*>(
+      static_cast<const unsigned char*>(j.src) + (int64_t)b * j.src_bstride);
+  uint4* __restrict__ dst = reinterpret_cast<uint4*>(
+      static_cast<unsigned char*>(j.dst) + (int64_t)b * j.dst_bstride);
+  const int64_t n16 = args->frame_bytes / 16;
+  const int64_t base = (int64_t)blockIdx.x * kCopyThreads * kCopyUnroll + threadIdx.x;
+  uint4 r[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = base + (int64_t)u * kCopyThreads;
+    r[u] = i < n16 ? src[i] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = base + (int64_t)u * kCopyThreads;
+    if (i < n16) dst[i] = r[u];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
+  if (a.n_jobs <= 0) return hipSuccess;
+  if (a.n_jobs > kMaxCopyJobs || a.frame_bytes % 16) return hipErrorInvalidValue;
+  const int64_t n16 = a.frame_bytes / 16;
+  const int64_t per_block = kCopyThreads * kCopyUnroll;
+  const dim3 grid((unsigned)((n16 + per_block - 1) / per_block), a.n_jobs, a.batch);
+  hipLaunchKernelGGL(copy_frames_kernel, grid, dim3(kCopyThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ca2

@@ -1,0 +1,58 @@
+// Device-side helpers shared by the gfx950 kernels of libca2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ca2 {
+
+typedef uint16_t bf16_t;  // bfloat16 storage (upper 16 bits of a float32)
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Two floats -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  bf16x2v b = __builtin_convertvector(f, bf16x2v);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Element-type traits: how many values one 16-byte chunk holds and how to
+// unpack / pack them to float32.
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+  static constexpr int kPerChunk = 4;
+  __device__ __forceinline__ static void unpack(const uint4& c, float* o) {
+    o[0] = __uint_as_float(c.x); o[1] = __uint_as_float(c.y);
+    o[2] = __uint_as_float(c.z); o[3] = __uint_as_float(c.w);
+  }
+  __device__ __forceinline__ static uint4 pack(const float* v) {
+    return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]),
+                      __float_as_uint(v[2]), __float_as_uint(v[3]));
+  }
+};
+
+template <> struct Elem<bf16_t> {
+  static constexpr int kPerChunk = 8;
+  __device__ __forceinline__ static void unpack(const uint4& c, float* o) {
+    o[0] = bf16_lo(c.x); o[1] = bf16_hi(c.x); o[2] = bf16_lo(c.y); o[3] = bf16_hi(c.y);
+    o[4] = bf16_lo(c.z); o[5] = bf16_hi(c.z); o[6] = bf16_lo(c.w); o[7] = bf16_hi(c.w);
+  }
+  __device__ __forceinline__ static uint4 pack(const float* v) {
+    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                      pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+  }
+};
+
+}  // namespace ca2

@@ -1,0 +1,78 @@
+// Internal launcher interface between the host state machine (ca2_host.cpp)
+// and the HIP kernels. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ca2 {
+
+// Causal temporal attention over the queue + new frames (one launch).
+struct TemporalArgs {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  void* out;
+  const void* ring_k;
+  const void* ring_v;
+  int32_t rows_total;      // B * S * H
+  int32_t rows_per_batch;  // S * H
+  int32_t n;               // new frames (queries per row)
+  int32_t p_k;             // queued frames
+  int32_t head;            // ring slot of the oldest queued frame
+  int32_t p_max;           // ring slots
+  float scale_log2e;       // softmax scale * log2(e)
+};
+
+// Spatial attention of every (b, frame, head), prefix or self mode.
+struct SpatialArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const void* sp_k;        // spatial buffer [B][P'][S][H][d]
+  const void* sp_v;
+  int32_t batch, n, tokens, heads;
+  int32_t p_slots;         // physical slots of the spatial buffer (P')
+  int32_t n_prefix;        // prefix frames used (0 in self mode)
+  int32_t prefix_slot[16]; // logical -> physical slot
+  float scale_log2e;
+};
+
+// Bitwise frame copies for the cache write. Job j copies `frame_elems`
+// elements for each batch entry b from src + b*src_bstride to
+// dst + b*dst_bstride (element offsets, 16-byte chunks).
+struct CopyJob {
+  const void* src;
+  void* dst;
+  int64_t src_bstride;  // bytes
+  int64_t dst_bstride;  // bytes
+};
+static constexpr int kMaxCopyJobs = 64;
+struct CopyArgs {
+  CopyJob job[kMaxCopyJobs];
+  int32_t n_jobs;
+  int32_t batch;
+  int64_t frame_bytes;
+};
+
+struct ProjArgs {
+  const void* x;
+  const void* w;
+  void* q;
+  void* k;
+  void* v;
+  int32_t m, c_in, c_out;
+};
+
+// Each launcher returns hipSuccess or the launch error; it returns
+// hipErrorInvalidValue for a (dtype, head_dim) pair that is not built.
+hipError_t launch_temporal(int dtype, int head_dim, const TemporalArgs& a, hipStream_t s);
+hipError_t launch_spatial(int dtype, int head_dim, const SpatialArgs& a, hipStream_t s);
+hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
+hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s);
+
+bool temporal_supported(int dtype, int head_dim);
+bool spatial_supported(int dtype, int head_dim);
+
+}  // namespace ca2

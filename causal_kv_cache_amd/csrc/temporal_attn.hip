@@ -1,0 +1,287 @@
+// Causal temporal attention over the shared temporal KV queue (gfx950).
+//
+// Computes, for every row (b, s, h) and new frame i < n, softmax over the
+// P_k queued frames plus new frames 0..i of scale * q_i . k, times V
+// (Ca2-VDM notes, key design 1: CausalAttn equation with a lower-triangular
+// mask; key design 4: the queue of at most P_max cached frames).
+//
+// Work mapping (HBM-bound: each K/V byte is used by at most n queries):
+//   * a wavefront owns ROWS = 64/QL consecutive rows; lane = (row, query),
+//     QL = lanes per row >= n, so the n queries of a row sit in adjacent
+//     lanes and read the same staged key row (LDS broadcast);
+//   * a workgroup is NW wavefronts on the same rows; the key frames are cut
+//     into blocks of F frames and dealt round-robin to the wavefronts, which
+//     run without block-wide barriers on wave-private LDS;
+//   * per block, the wavefront copies F frames x ROWS rows of K and V from
+//     HBM into its LDS slice with 16-byte loads: for one frame the ROWS rows
+//     are contiguous (heads innermost), so a wavefront reads whole runs of
+//     ROWS*d*elem bytes;
+//   * online softmax in base 2 with one rescale per block; partial
+//     (max, sum, acc) of the NW wavefronts are merged through LDS at the end.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace ca2 {
+namespace {
+
+constexpr int kWaves = 4;              // wavefronts per workgroup
+constexpr int kStageBudget = 20480;    // LDS bytes per wavefront for K+V staging
+
+template <typename T, int D, int QL>
+struct TCfg {
+  static constexpr int ROWS = 64 / QL;
+  static constexpr int EB = (int)sizeof(T);
+  static constexpr int VPC = Elem<T>::kPerChunk;       // values per 16-byte chunk
+  static constexpr int CPR = D * EB / 16;              // chunks per row
+  static constexpr int FRAME_BYTES = ROWS * D * EB;    // one frame of the wave's rows
+  static constexpr int F_RAW = kStageBudget / (2 * FRAME_BYTES);
+  static constexpr int F = F_RAW >= 8 ? 8 : F_RAW >= 4 ? 4 : F_RAW >= 2 ? 2 : 1;
+  static constexpr int CHUNKS = F * ROWS * CPR;        // per tensor per block
+  static constexpr int CPL = (CHUNKS + 63) / 64;       // chunks per lane
+  static constexpr int STAGE_U4 = 2 * CHUNKS;          // uint4 per wave (K then V)
+  static constexpr int MERGE_F = 64 * (D + 2);         // floats per wave for the merge
+  static constexpr int LDS_U4_STAGE = kWaves * STAGE_U4;
+  static constexpr int LDS_U4_MERGE = ((kWaves - 1) * MERGE_F * 4 + 15) / 16;
+  static constexpr int LDS_U4 = LDS_U4_STAGE > LDS_U4_MERGE ? LDS_U4_STAGE : LDS_U4_MERGE;
+  static_assert(D * EB % 16 == 0, "row must be a whole number of 16-byte chunks");
+};
+
+template <typename T, int D, int QL>
+__global__ __launch_bounds__(64 * kWaves) void temporal_attn_kernel(TemporalArgs a) {
+  using C = TCfg<T, D, QL>;
+  constexpr int ROWS = C::ROWS, CPR = C::CPR, F = C::F, CHUNKS = C::CHUNKS, CPL = C::CPL;
+  constexpr int VPC = C::VPC;
+  __shared__ uint4 lds[C::LDS_U4];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row0 = blockIdx.x * ROWS;
+  const int ri = lane / QL;
+  const int qi = lane % QL;
+  const int row = row0 + ri;
+  const bool active = row < a.rows_total && qi < a.n;
+  const int rpb = a.rows_per_batch;
+
+  const T* __restrict__ qp = static_cast<const T*>(a.q);
+  const T* __restrict__ knp = static_cast<const T*>(a.k_new);
+  const T* __restrict__ vnp = static_cast<const T*>(a.v_new);
+  const T* __restrict__ rkp = static_cast<const T*>(a.ring_k);
+  const T* __restrict__ rvp = static_cast<const T*>(a.ring_v);
+
+  // ---- this lane's query, in float32 registers --------------------------
+  float qf[D];
+  {
+    const int b = row / rpb, rr = row % rpb;
+    const int64_t off = ((int64_t)(b * a.n + qi) * rpb + rr) * D;
+#pragma unroll
+    for (int c = 0; c < CPR; ++c) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (active) u = *reinterpret_cast<const uint4*>(qp + off + c * VPC);
+      Elem<T>::unpack(u, qf + c * VPC);
+    }
+  }
+
+  // ---- per-chunk staging coordinates (same every block) -----------------
+  // chunk e of a block = (frame fo, row r, piece cc) with e = (fo*ROWS + r)*CPR + cc
+  int64_t ch_rowoff[CPL];   // element offset of (row, piece) inside a frame of its batch
+  int ch_b[CPL], ch_fo[CPL];
+  bool ch_ok[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int e = c * 64 + lane;
+    const int fo = e / (ROWS * CPR);
+    const int rem = e % (ROWS * CPR);
+    const int r = rem / CPR, cc = rem % CPR;
+    const int grow = row0 + r;
+    ch_ok[c] = e < CHUNKS && grow < a.rows_total;
+    const int b = grow / rpb, rr = grow % rpb;
+    ch_b[c] = b;
+    ch_fo[c] = fo;
+    ch_rowoff[c] = (int64_t)rr * D + cc * VPC;
+  }
+
+  uint4* stage = lds + wave * C::STAGE_U4;
+  const int k_total = a.p_k + a.n;
+  const int n_blocks = (k_total + F - 1) / F;
+  const int last_key = a.p_k + qi;          // keys 0..last_key are visible
+  const int64_t frame_elems = (int64_t)rpb * D;
+
+  float m = -INFINITY, l = 0.f;
+  float acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) acc[d] = 0.f;
+
+  for (int blk = wave; blk < n_blocks; blk += kWaves) {
+    const int j0 = blk * F;
+    // -- stage F key frames (K then V) of this wave's rows into LDS --
+    uint4 kr[CPL], vr[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int j = j0 + ch_fo[c];
+      kr[c] = make_uint4(0, 0, 0, 0);
+      vr[c] = make_uint4(0, 0, 0, 0);
+      if (ch_ok[c] && j < k_total) {
+        const T* kb;
+        const T* vb;
+        int64_t base;
+        if (j < a.p_k) {
+          int slot = a.head + j;
+          if (slot >= a.p_max) slot -= a.p_max;
+          base = ((int64_t)ch_b[c] * a.p_max + slot) * frame_elems;
+          kb = rkp; vb = rvp;
+        } else {
+          base = ((int64_t)ch_b[c] * a.n + (j - a.p_k)) * frame_elems;
+          kb = knp; vb = vnp;
+        }
+        kr[c] = *reinterpret_cast<const uint4*>(kb + base + ch_rowoff[c]);
+        vr[c] = *reinterpret_cast<const uint4*>(vb + base + ch_rowoff[c]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int e = c * 64 + lane;
+      if (e < CHUNKS) {
+        stage[e] = kr[c];
+        stage[CHUNKS + e] = vr[c];
+      }
+    }
+    // LDS accesses of one wavefront complete in order; this only stops the
+    // compiler from moving the reads above the writes.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // -- scores of the block --
+    float sc[F];
+    float mb = -INFINITY;
+#pragma unroll
+    for (int fo = 0; fo < F; ++fo) {
+      const uint4* krow = stage + (fo * ROWS + ri) * CPR;
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPR; ++c) {
+        float kv[VPC];
+        Elem<T>::unpack(krow[c], kv);
+#pragma unroll
+        for (int e = 0; e < VPC; ++e) s = fmaf(qf[c * VPC + e], kv[e], s);
+      }
+      const int j = j0 + fo;
+      const bool vis = active && j <= last_key && j < k_total;
+      sc[fo] = vis ? s * a.scale_log2e : -INFINITY;
+      mb = fmaxf(mb, sc[fo]);
+    }
+    const float m_new = fmaxf(m, mb);
+    if (m_new != -INFINITY) {
+      const float corr = fast_exp2(m - m_new);   // 0 when m was -inf
+      l *= corr;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] *= corr;
+#pragma unroll
+      for (int fo = 0; fo < F; ++fo) {
+        const float p = fast_exp2(sc[fo] - m_new);   // 0 for hidden keys
+        l += p;
+        const uint4* vrow = stage + CHUNKS + (fo * ROWS + ri) * CPR;
+#pragma unroll
+        for (int c = 0; c < CPR; ++c) {
+          float vv[VPC];
+          Elem<T>::unpack(vrow[c], vv);
+#pragma unroll
+          for (int e = 0; e < VPC; ++e) acc[c * VPC + e] = fmaf(p, vv[e], acc[c * VPC + e]);
+        }
+      }
+      m = m_new;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- merge the wavefronts' partial results -------------------------------
+  __syncthreads();   // staging slices are reused for the merge
+  float* mf = reinterpret_cast<float*>(lds);
+  if (wave > 0) {
+    float* dst = mf + (wave - 1) * C::MERGE_F + lane;
+    dst[0] = m;
+    dst[64] = l;
+#pragma unroll
+    for (int d = 0; d < D; ++d) dst[(d + 2) * 64] = acc[d];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float mw[kWaves];
+    mw[0] = m;
+    float m_all = m;
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      mw[w] = mf[(w - 1) * C::MERGE_F + lane];
+      m_all = fmaxf(m_all, mw[w]);
+    }
+    if (active && m_all != -INFINITY) {
+      const float s0 = fast_exp2(m - m_all);
+      float lt = l * s0;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] *= s0;
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        const float* src = mf + (w - 1) * C::MERGE_F + lane;
+        const float sw = fast_exp2(mw[w] - m_all);   // 0 for a wave with no visible key
+        lt = fmaf(src[64], sw, lt);
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc[d] = fmaf(src[(d + 2) * 64], sw, acc[d]);
+      }
+      const float inv = 1.f / lt;
+      T* op = static_cast<T*>(a.out);
+      const int b = row / rpb, rr = row % rpb;
+      const int64_t off = ((int64_t)(b * a.n + qi) * rpb + rr) * D;
+#pragma unroll
+      for (int c = 0; c < CPR; ++c) {
+        float o[VPC];
+#pragma unroll
+        for (int e = 0; e < VPC; ++e) o[e] = acc[c * VPC + e] * inv;
+        *reinterpret_cast<uint4*>(op + off + c * VPC) = Elem<T>::pack(o);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_td(const TemporalArgs& a, hipStream_t s) {
+  const int ql = a.n <= 4 ? 4 : a.n <= 8 ? 8 : 16;
+  const int rows = 64 / ql;
+  const dim3 grid((a.rows_total + rows - 1) / rows);
+  const dim3 block(64 * kWaves);
+  if (ql == 4) hipLaunchKernelGGL((temporal_attn_kernel<T, D, 4>), grid, block, 0, s, a);
+  else if (ql == 8) hipLaunchKernelGGL((temporal_attn_kernel<T, D, 8>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((temporal_attn_kernel<T, D, 16>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool temporal_supported(int dtype, int d) {
+  if (dtype == 0) return d == 16 || d == 32 || d == 64 || d == 72 || d == 128;
+  if (dtype == 1) return d == 64 || d == 72 || d == 128;
+  return false;
+}
+
+hipError_t launch_temporal(int dtype, int d, const TemporalArgs& a, hipStream_t s) {
+  if (a.n < 1 || a.n > 16) return hipErrorInvalidValue;
+  if (dtype == 0) {
+    switch (d) {
+      case 16: return launch_td<float, 16>(a, s);
+      case 32: return launch_td<float, 32>(a, s);
+      case 64: return launch_td<float, 64>(a, s);
+      case 72: return launch_td<float, 72>(a, s);
+      case 128: return launch_td<float, 128>(a, s);
+    }
+  } else if (dtype == 1) {
+    switch (d) {
+      case 64: return launch_td<bf16_t, 64>(a, s);
+      case 72: return launch_td<bf16_t, 72>(a, s);
+      case 128: return launch_td<bf16_t, 128>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ca2

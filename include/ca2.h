@@ -1,0 +1,213 @@
+/*
+ * ca2.h -- C ABI of libca2: shared causal KV-cache attention for
+ * autoregressive video diffusion (Ca2-VDM), on AMD MI355X (gfx950).
+ *
+ * Source pages cited below:
+ *   [notes]    papernotes.org, "Ca2-VDM: Efficient Autoregressive Video Diffusion
+ *              Model with Causal Generation and Cache Sharing" (ICML 2025 notes).
+ *              Sections: overall framework (整体框架), key designs 1-5 (关键设计),
+ *              training strategy, GPU-memory table.
+ *   [abstract] bohrium.dp.tech abstract page of arXiv 2411.16375, section
+ *              "Formula Representation".
+ *
+ * What the library holds: one cache object per (layer, batch) = a temporal
+ * KV ring of P_max frame slots ([notes] key design 4: FIFO queue capped at
+ * P_max) plus a spatial KV buffer of P' frame slots ([notes] key design 5:
+ * one chunk's spatial K/V, overwritten every autoregressive step). The cache is
+ * read by every denoising call and written only by ca2_cache_write, so one
+ * copy serves all T denoising steps ([notes] key design 2, cache sharing).
+ *
+ * Conventions (all entry points):
+ *   - Layout of every activation tensor: [B][n][S][H][d] contiguous
+ *     (batch, frame, spatial token, head, head dim); the ring is
+ *     [B][P_max][S][H][d] and the spatial buffer [B][P'][S][H][d].
+ *   - Device pointers are owned by the caller, must be 16-byte aligned and
+ *     must not alias the output. The library never frees them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = legacy default stream).
+ *     Every compute call is asynchronous on that stream. Host-side cache state
+ *     (queue head, P_k, frames written) is updated when the call is enqueued,
+ *     so later calls must be ordered after earlier ones on the device (same
+ *     stream, or caller-managed events).
+ *   - Arguments are validated before anything is launched; on error nothing
+ *     is enqueued, the state is unchanged, and ca2_last_error() gives detail.
+ *     No call aborts or throws across the ABI.
+ *   - Dtypes: CA2_F32 (float) or CA2_BF16 (bfloat16 storage); accumulation,
+ *     softmax statistics and the normaliser are float32 in both.
+ */
+#ifndef CA2_H
+#define CA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ca2_cache ca2_cache;   /* opaque; owns its ring + spatial HBM buffers */
+
+typedef enum {
+  CA2_OK = 0,
+  CA2_ERR_INVALID_ARG = 1,   /* bad pointer, size, alignment or config */
+  CA2_ERR_OUT_OF_MEMORY = 2, /* hipMalloc failed at create */
+  CA2_ERR_HIP = 3,           /* a HIP runtime call failed (see ca2_last_error) */
+  CA2_ERR_STATE = 4,         /* call not valid in the cache's current state */
+  CA2_ERR_UNSUPPORTED = 5    /* valid but not built (e.g. head_dim) */
+} ca2_status;
+
+typedef enum { CA2_F32 = 0, CA2_BF16 = 1 } ca2_dtype;
+
+typedef enum {
+  CA2_SPATIAL_PREFIX = 0,    /* keys = own frame + the P' cached frames */
+  CA2_SPATIAL_SELF = 1       /* keys = own frame only */
+} ca2_spatial_mode;
+
+typedef struct {
+  int32_t batch;       /* B >= 1 */
+  int32_t heads;       /* H >= 1 */
+  int32_t head_dim;    /* d: f32 {16,32,64,72,128}, bf16 {64,72,128} */
+  int32_t tokens;      /* S = HW latent tokens per frame, >= 1 */
+  int32_t chunk;       /* l: frames per autoregressive chunk, 1..16 */
+  int32_t p_max;       /* temporal queue capacity P_max >= 1 */
+  int32_t p_spatial;   /* spatial prefix frames P', 0 <= P' < l */
+  int32_t tpe_len;     /* cyclic TPE table length, >= p_max + chunk */
+  int32_t dtype;       /* ca2_dtype */
+} ca2_config;
+
+typedef struct {
+  int32_t p_k;              /* frames in the temporal queue, min(frames_written, p_max) */
+  int32_t head_slot;        /* ring slot of the oldest queued frame */
+  int32_t spatial_frames;   /* distinct clean frames held by the spatial buffer */
+  int32_t reserved;
+  int64_t frames_written;   /* clean frames ever written */
+  uint64_t bytes_resident;  /* device bytes of ring + spatial buffer */
+} ca2_cache_info;
+
+/*
+ * Create a cache for `cfg`: allocates the ring (2 * B*P_max*S*H*d elements)
+ * and the spatial buffer (2 * B*P'*S*H*d) once; nothing is reallocated later.
+ * Starts empty (frames_written = 0). Checks P' < l ([notes] key design 5
+ * relies on it) and tpe_len >= p_max + chunk (so every window of queued plus
+ * new frames has distinct TPE indices, [notes] key design 4).
+ * Errors: INVALID_ARG (null, bad config), UNSUPPORTED (head_dim/dtype pair
+ * not built), OUT_OF_MEMORY, HIP. On error *out is set to NULL.
+ */
+ca2_status ca2_cache_create(const ca2_config* cfg, ca2_cache** out);
+
+/* Free the cache's device buffers and the object. NULL-safe. The caller must
+ * make sure no enqueued work still uses the cache. */
+void ca2_cache_destroy(ca2_cache* cache);
+
+/*
+ * Cache-writing stage ([notes] overall framework: after denoising, one pass
+ * of the clean chunk at t = 0 computes K/V that are stored for later steps).
+ * k_t, v_t: temporal-layer K/V of the n clean frames, [B][n][S][H][d].
+ * k_s, v_s: spatial-layer K/V of the same frames, [B][n][S][H][d]; may be
+ *           NULL only when p_spatial == 0.
+ * Appends the frames to the temporal queue -- frame F goes to ring slot
+ * F mod P_max, which is the slot right after the newest queued frame -- and,
+ * past P_max, drops the oldest frames (FIFO eviction, [notes] key design 4).
+ * An over-full write is the normal case, not an error. Keeps the last P'
+ * clean frames in the spatial buffer (frame F at slot F mod P'). Copies are
+ * bitwise. 1 <= n_frames <= chunk. Enqueue this after the cache-writing
+ * pass's attention calls: they must see the queue before eviction.
+ */
+ca2_status ca2_cache_write(ca2_cache* cache, const void* k_t, const void* v_t,
+                           const void* k_s, const void* v_s, int32_t n_frames,
+                           void* stream);
+
+/*
+ * Causal temporal attention ([notes] key design 1, CausalAttn equation with
+ * its lower-triangular mask; [abstract] Formula Representation).
+ * For each row (b, s, h) and new frame i in [0, n): keys/values are the P_k
+ * queued frames (oldest first) followed by new frames 0..i; out_i =
+ * softmax(scale * q_i . K^T) V over exactly those P_k + i + 1 keys.
+ * q, k_new, v_new, out: [B][n][S][H][d] in the cache's dtype.
+ * 1 <= n_frames <= chunk; scale > 0 and finite (normally 1/sqrt(d)).
+ * Reads the cache, never writes it.
+ */
+ca2_status ca2_temporal_attn(const ca2_cache* cache, const void* q, const void* k_new,
+                             const void* v_new, void* out, int32_t n_frames,
+                             float scale, void* stream);
+
+/*
+ * Spatial attention of each of the n frames ([notes] key design 3).
+ * CA2_SPATIAL_PREFIX: keys/values of frame f are its own S tokens followed by
+ *   the S tokens of each of the P' spatial-buffer frames (oldest first), a
+ *   map of S x (P'+1)S. While fewer than P' clean frames exist the oldest one
+ *   fills the missing positions. Needs frames_written >= 1 (else STATE).
+ * CA2_SPATIAL_SELF: keys/values are the frame's own S tokens (the clean-frame
+ *   self-repeat case, whose value equals plain self-attention).
+ * q, k, v, out: [B][n][S][H][d]. 1 <= n_frames <= chunk.
+ */
+ca2_status ca2_spatial_attn(const ca2_cache* cache, const void* q, const void* k,
+                            const void* v, void* out, int32_t n_frames, int32_t mode,
+                            float scale, void* stream);
+
+/*
+ * Cyclic TPE indices of the next n frames ([notes] key design 4,
+ * Cyclic-TPEs): host_out[i] = (frames_written + i) mod tpe_len, frame 0 being
+ * the conditioning frame. Host-only; host_out has n_frames entries.
+ */
+ca2_status ca2_tpe_index(const ca2_cache* cache, int32_t n_frames, int32_t* host_out);
+
+/* Same arithmetic without a cache (pure host function, no GPU needed). */
+ca2_status ca2_tpe_index_raw(int64_t first_frame, int32_t n, int32_t tpe_len,
+                             int32_t* host_out);
+
+/* Snapshot of the host-side state. */
+ca2_status ca2_cache_info_get(const ca2_cache* cache, ca2_cache_info* out);
+
+/* Ring slot of each logical queue position, oldest first: host_out[p_k]. */
+ca2_status ca2_cache_slot_map(const ca2_cache* cache, int32_t* host_out);
+
+/* Absolute frame ids held: temporal_out[p_k] oldest first (may be NULL);
+ * spatial_out[p_spatial] in logical order, padded with the oldest frame while
+ * fewer than P' exist (may be NULL); spatial_slots_out[p_spatial] the buffer
+ * slot of each logical position (may be NULL). */
+ca2_status ca2_cache_frame_ids(const ca2_cache* cache, int64_t* temporal_out,
+                               int64_t* spatial_out, int32_t* spatial_slots_out);
+
+/* Pure host versions of the slot arithmetic, for CPU tests:
+ * ring: p_k = min(frames_written, p_max); slot of logical j =
+ * (frames_written - p_k + j) mod p_max; host_out has p_max entries (p_k used).
+ * spatial: logical j holds frame max(0, frames_written - p_spatial + j),
+ * slot = frame mod p_spatial; frames_out/slots_out have p_spatial entries. */
+ca2_status ca2_ring_slot_map_raw(int64_t frames_written, int32_t p_max,
+                                 int32_t* host_out, int32_t* p_k_out);
+ca2_status ca2_spatial_slot_map_raw(int64_t frames_written, int32_t p_spatial,
+                                    int64_t* frames_out, int32_t* slots_out);
+
+/* Bytes the cache for `cfg` holds on the device: 2 * B * (P_max + P') * S *
+ * H * d * elem ([notes] GPU-memory table: independent of T). 0 if cfg is
+ * invalid. Pure host function. */
+uint64_t ca2_bytes_resident(const ca2_config* cfg);
+
+/* Synchronous copy of the whole ring and spatial buffer to host memory
+ * (physical slot order). Any of the pointers may be NULL. Sizes:
+ * host_k/host_v B*P_max*S*H*d elements, host_ks/host_vs B*P'*S*H*d. */
+ca2_status ca2_cache_debug_copy(const ca2_cache* cache, void* host_k, void* host_v,
+                                void* host_ks, void* host_vs, void* stream);
+
+/*
+ * QKV projection of the clean chunk for the cache-writing stage ([notes]
+ * overall framework: one forward pass of the denoised chunk produces the K/V
+ * that are stored). x: [m][c_in] bf16 tokens; w: [3*c_out][c_in] bf16,
+ * row-major weight of a linear layer; q, k, v: [m][c_out] bf16 outputs =
+ * columns [0,c), [c,2c), [2c,3c) of x * w^T, accumulated in float32.
+ * m >= 1; c_in and c_out multiples of 64.
+ */
+ca2_status ca2_qkv_proj(const void* x, const void* w, void* q, void* k, void* v,
+                        int32_t m, int32_t c_in, int32_t c_out, void* stream);
+
+/* Static description of a status code. */
+const char* ca2_status_string(ca2_status status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* ca2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CA2_H */

@@ -118,9 +118,12 @@ def spatial_attn_ref(q, k, v, ks, vs, prefix_slots, scale, mode):
         kf = _spatial_keys(k[:, f], ks, prefix_slots, mode)   # [B][Sk][H][d]
         vf = _spatial_keys(v[:, f], vs, prefix_slots, mode)
         for b in range(B):
-            z = scale * np.einsum("shd,thd->hst", q[b, f], kf[b])
+            qh = q[b, f].transpose(1, 0, 2)          # [H][S_q][d]
+            kh = kf[b].transpose(1, 2, 0)            # [H][d][S_k]
+            vh = vf[b].transpose(1, 0, 2)            # [H][S_k][d]
+            z = scale * np.matmul(qh, kh)            # [H][S_q][S_k]
             p = softmax_rows(z)
-            out[b, f] = np.einsum("hst,thd->shd", p, vf[b])
+            out[b, f] = np.matmul(p, vh).transpose(1, 0, 2)
     return out
 
 

@@ -81,7 +81,7 @@ class RolloutOracle:
                                  self.queue.slot_map(), self.scale)
 
     def spatial_out(self, q, k, v, mode):
-        if mode == "prefix":
+        if mode == "prefix" and self.sh["p_spatial"] > 0:
             ks, vs, slots = self.spatial_prefix()
             if not slots:
                 raise RuntimeError("prefix mode needs at least one clean frame")

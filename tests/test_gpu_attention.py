@@ -1,0 +1,185 @@
+"""GPU parity of the temporal (K1) and spatial (K2) attention kernels against
+the oracle, through the C ABI. fp32: |g-o| <= 1e-5|o| + 1e-6; bf16: max-abs
+<= 2e-2. Shapes span several workgroup tiles and ragged tails; the full-size
+workloads are checked in the launch configuration the benchmark uses."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import RolloutOracle, temporal_attn_ref, spatial_attn_ref
+from gpu_util import to_dev, to_host, empty_like_dev, check_close
+
+pytestmark = pytest.mark.gpu
+
+
+def shape_of(B, H, d, S, l, p_max, p_spatial, dtype, tpe_len=None):
+    return dict(B=B, H=H, d=d, S=S, l=l, p_max=p_max, p_spatial=p_spatial,
+                tpe_len=tpe_len or p_max + l, dtype=dtype)
+
+
+def fill(ca2, sh, seed, writes):
+    """A cache and its oracle after writing clean frames in chunks ``writes``."""
+    cache = ca2.Cache.from_shape(sh)
+    o = RolloutOracle(sh, seed)
+    dt = sh["dtype"]
+    for w in writes:
+        frames = o.next_frames(w)
+        kt, vt, ks, vs = (to_dev(o.clean(x, frames), dt) for x in ("kt", "vt", "ks", "vs"))
+        cache.ca2_cache_write(kt, vt, ks, vs)
+        o.write(frames)
+    torch.cuda.synchronize()
+    return cache, o
+
+
+TEMPORAL_CASES = [
+    # (name, shape, writes, n)
+    ("tiny_f32_full_wrapped", shape_of(1, 2, 16, 16, 4, 9, 1, "f32", 13), [1, 4, 4, 4], 4),
+    ("tiny_f32_full_n1", shape_of(1, 2, 16, 16, 4, 9, 1, "f32", 13), [1, 4, 4, 4], 1),
+    ("tiny_f32_growing", shape_of(1, 2, 16, 16, 4, 9, 1, "f32", 13), [1, 4], 3),
+    ("tiny_f32_empty", shape_of(1, 2, 16, 16, 4, 9, 1, "f32", 13), [], 4),
+    ("f32_d72_ragged", shape_of(2, 3, 72, 5, 8, 25, 3, "f32"), [1, 8, 8, 8, 8], 8),
+    ("f32_d32", shape_of(1, 4, 32, 9, 4, 9, 1, "f32"), [1, 4, 4, 4, 4], 4),
+    ("f32_d64", shape_of(1, 3, 64, 7, 8, 9, 1, "f32"), [1, 8, 8], 5),
+    ("f32_d128", shape_of(1, 2, 128, 6, 16, 17, 3, "f32"), [1, 16, 16], 16),
+    ("bf16_d72_ragged", shape_of(2, 3, 72, 5, 8, 25, 3, "bf16"), [1, 8, 8, 8, 8], 8),
+    ("bf16_d72_ragged_n3", shape_of(2, 3, 72, 5, 8, 25, 3, "bf16"), [1, 8, 8, 8, 8], 3),
+    ("bf16_d72_n16", shape_of(1, 5, 72, 7, 16, 33, 3, "bf16"), [1, 16, 16, 16], 16),
+    ("bf16_d72_empty", shape_of(1, 16, 72, 16, 8, 25, 3, "bf16"), [], 1),
+    ("bf16_d64", shape_of(1, 4, 64, 33, 8, 25, 3, "bf16"), [1, 8, 8, 8, 8], 8),
+    ("bf16_d128", shape_of(1, 2, 128, 40, 8, 17, 3, "bf16"), [1, 8, 8, 8], 6),
+]
+
+
+@pytest.mark.parametrize("name,sh,writes,n", TEMPORAL_CASES, ids=[c[0] for c in TEMPORAL_CASES])
+def test_temporal_parity_small(ca2, name, sh, writes, n):
+    cache, o = fill(ca2, sh, 100, writes)
+    q, k, v = (o.noisy(x, 1, 7, n) for x in ("q", "k", "v"))
+    out = empty_like_dev((sh["B"], n, sh["S"], sh["H"], sh["d"]), sh["dtype"])
+    cache.ca2_temporal_attn(to_dev(q, sh["dtype"]), to_dev(k, sh["dtype"]), to_dev(v, sh["dtype"]), out)
+    torch.cuda.synchronize()
+    ref = temporal_attn_ref(q, k, v, o.ring_k, o.ring_v, o.queue.slot_map(), o.scale)
+    check_close(to_host(out), ref, sh["dtype"], name)
+
+
+def test_temporal_ar_step_s256_full(ca2):
+    """One denoising call at the 256-token shape, queue full (P_k = 25), every output checked."""
+    sh = synth.WORKLOADS["ar_step_s256"]
+    cache, o = fill(ca2, sh, 7, [1, 8, 8, 8])
+    assert cache.ca2_cache_info_get()["p_k"] == 25
+    q, k, v = (o.noisy(x, 4, 50, 8) for x in ("q", "k", "v"))
+    out = empty_like_dev(q.shape, "bf16")
+    cache.ca2_temporal_attn(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), out)
+    torch.cuda.synchronize()
+    ref = temporal_attn_ref(q, k, v, o.ring_k, o.ring_v, o.queue.slot_map(), o.scale)
+    check_close(to_host(out), ref, "bf16", "ar_step_s256 temporal")
+
+
+def test_temporal_v_ones_is_exact_one(ca2):
+    sh = shape_of(1, 16, 72, 32, 8, 25, 3, "bf16")
+    cache = ca2.Cache.from_shape(sh)
+    g = np.random.default_rng(0)
+    for w in (1, 8, 8, 8, 8):
+        kt = synth.round_to_bf16(g.standard_normal((1, w, 32, 16, 72)).astype(np.float32) * 3)
+        ones = np.ones_like(kt)
+        cache.ca2_cache_write(to_dev(kt, "bf16"), to_dev(ones, "bf16"), to_dev(kt, "bf16"), to_dev(ones, "bf16"))
+    q = synth.round_to_bf16(g.standard_normal((1, 8, 32, 16, 72)).astype(np.float32) * 3)
+    out = empty_like_dev(q.shape, "bf16")
+    cache.ca2_temporal_attn(to_dev(q, "bf16"), to_dev(q, "bf16"), to_dev(np.ones_like(q), "bf16"), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out), np.ones(q.shape))
+
+
+def test_temporal_never_reads_unwritten_slots(ca2, monkeypatch):
+    """Ring filled with NaN before any write: a partly filled queue must give finite outputs."""
+    monkeypatch.setenv("CA2_NAN_CANARY", "1")
+    sh = shape_of(1, 4, 72, 24, 8, 25, 3, "bf16")
+    cache, o = fill(ca2, sh, 3, [1, 8])
+    ring = cache.ca2_cache_debug_copy()[0]
+    assert np.all(ring[:, 9:] == 0xFFFF)       # slots 9.. still hold the canary
+    q, k, v = (o.noisy(x, 2, 3, 8) for x in ("q", "k", "v"))
+    out = empty_like_dev(q.shape, "bf16")
+    cache.ca2_temporal_attn(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), out)
+    torch.cuda.synchronize()
+    ref = temporal_attn_ref(q, k, v, o.ring_k, o.ring_v, o.queue.slot_map(), o.scale)
+    check_close(to_host(out), ref, "bf16", "canary temporal")
+
+
+SPATIAL_CASES = [
+    # (name, shape, writes, n, mode)
+    ("tiny_f32_prefix_clamp", shape_of(1, 2, 16, 16, 4, 9, 1, "f32", 13), [1], 4, 0),
+    ("tiny_f32_prefix", shape_of(1, 2, 16, 16, 4, 9, 1, "f32", 13), [1, 4, 4], 4, 0),
+    ("tiny_f32_self", shape_of(1, 2, 16, 16, 4, 9, 1, "f32", 13), [1, 4], 4, 1),
+    ("f32_d72_ragged_prefix", shape_of(2, 3, 72, 70, 8, 25, 3, "f32"), [1, 8], 3, 0),
+    ("f32_d128_self", shape_of(1, 2, 128, 65, 8, 25, 3, "f32"), [1], 2, 1),
+    ("bf16_d72_ragged_prefix_clamp", shape_of(2, 3, 72, 200, 8, 25, 3, "bf16"), [1], 8, 0),
+    ("bf16_d72_ragged_prefix", shape_of(2, 3, 72, 200, 8, 25, 3, "bf16"), [1, 8, 1], 8, 0),
+    ("bf16_d72_ragged_self", shape_of(2, 3, 72, 200, 8, 25, 3, "bf16"), [1, 8], 5, 1),
+    ("bf16_d72_p0", shape_of(1, 2, 72, 130, 4, 9, 0, "bf16"), [1, 4], 4, 0),
+    ("bf16_d72_tiny_tokens", shape_of(1, 3, 72, 9, 4, 9, 2, "bf16"), [1, 4], 4, 0),
+    ("bf16_d64_prefix", shape_of(1, 4, 64, 192, 8, 25, 3, "bf16"), [1, 8], 8, 0),
+    ("bf16_d128_prefix", shape_of(1, 2, 128, 100, 8, 25, 2, "bf16"), [1, 8], 4, 0),
+]
+
+
+@pytest.mark.parametrize("name,sh,writes,n,mode", SPATIAL_CASES, ids=[c[0] for c in SPATIAL_CASES])
+def test_spatial_parity_small(ca2, name, sh, writes, n, mode):
+    cache, o = fill(ca2, sh, 200, writes)
+    q, k, v = (o.noisy(x, 1, 9, n) for x in ("q", "k", "v"))
+    out = empty_like_dev(q.shape, sh["dtype"])
+    cache.ca2_spatial_attn(to_dev(q, sh["dtype"]), to_dev(k, sh["dtype"]), to_dev(v, sh["dtype"]), out, mode=mode)
+    torch.cuda.synchronize()
+    ref = o.spatial_out(q, k, v, "prefix" if mode == 0 else "self")
+    check_close(to_host(out), ref, sh["dtype"], name)
+
+
+def test_spatial_ar_step_s256_full(ca2):
+    sh = synth.WORKLOADS["ar_step_s256"]
+    cache, o = fill(ca2, sh, 8, [1, 8, 8, 8])
+    q, k, v = (o.noisy(x, 4, 50, 8) for x in ("q", "k", "v"))
+    out = empty_like_dev(q.shape, "bf16")
+    cache.ca2_spatial_attn(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), out)
+    torch.cuda.synchronize()
+    ref = o.spatial_out(q, k, v, "prefix")
+    check_close(to_host(out), ref, "bf16", "ar_step_s256 spatial")
+
+
+def test_spatial_v_ones(ca2):
+    sh = shape_of(1, 2, 72, 256, 8, 25, 3, "bf16")
+    cache = ca2.Cache.from_shape(sh)
+    g = np.random.default_rng(1)
+    kt = synth.round_to_bf16(g.standard_normal((1, 8, 256, 2, 72)).astype(np.float32) * 3)
+    ones = np.ones_like(kt)
+    cache.ca2_cache_write(to_dev(kt, "bf16"), to_dev(ones, "bf16"), to_dev(kt, "bf16"), to_dev(ones, "bf16"))
+    out = empty_like_dev(kt.shape, "bf16")
+    cache.ca2_spatial_attn(to_dev(kt, "bf16"), to_dev(kt, "bf16"), to_dev(ones, "bf16"), out)
+    torch.cuda.synchronize()
+    # P is rounded to bf16 for the PV product while the normaliser stays fp32
+    assert np.max(np.abs(to_host(out) - 1.0)) <= 2.0 ** -7
+
+
+def test_large_b8_s1024_sampled(ca2):
+    """Batched 32x32-latent workload at full size: both kernels in their
+    benchmark launch configuration, outputs sampled over tokens (rows are
+    independent, so the oracle runs on those tokens only)."""
+    sh = synth.WORKLOADS["large_b8_s1024"]
+    cache, o = fill(ca2, sh, 9, [1, 8, 8, 8])
+    q, k, v = (o.noisy(x, 4, 50, 8) for x in ("q", "k", "v"))
+    dq, dk, dv = (to_dev(x, "bf16") for x in (q, k, v))
+    ot = empty_like_dev(q.shape, "bf16")
+    os_ = empty_like_dev(q.shape, "bf16")
+    cache.ca2_temporal_attn(dq, dk, dv, ot)
+    cache.ca2_spatial_attn(dq, dk, dv, os_)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(5)
+    toks = np.unique(np.concatenate([[0, 1, 63, 64, 511, 1022, 1023], g.integers(0, 1024, 25)]))
+    # temporal: slice tokens of every operand
+    ref_t = temporal_attn_ref(q[:, :, toks], k[:, :, toks], v[:, :, toks],
+                              o.ring_k[:, :, toks], o.ring_v[:, :, toks], o.queue.slot_map(), o.scale)
+    check_close(to_host(ot)[:, :, toks], ref_t, "bf16", "large temporal")
+    # spatial: slice query tokens only (keys stay whole); two batch entries, all frames/heads
+    for b in (0, 7):
+        ks, vs, slots = o.spatial_prefix()
+        ref_s = spatial_attn_ref(q[b:b + 1, :, toks], k[b:b + 1], v[b:b + 1], ks[b:b + 1], vs[b:b + 1],
+                                 slots, o.scale, "prefix")
+        check_close(to_host(os_)[b:b + 1, :, toks], ref_s, "bf16", f"large spatial b={b}")
