@@ -1,0 +1,323 @@
+"""Benchmark of the shared-cache attention hot path on one MI355X.
+
+A step is one autoregressive step at the 256-token Ca2-VDM shape (B=1, 16
+heads x 72, 16x16 latent tokens, chunk l=8, queue full at P_max=25, P'=3,
+bf16): 50 denoising calls -- each a prefix-enhanced spatial attention and a
+causal temporal attention over the shared cache, with fresh Q/K/V per call --
+then the cache-writing pass: spatial self attention, temporal attention of the
+clean chunk, and the cache write (append + FIFO evict + spatial overwrite).
+Inputs are synthetic (seeded N(0,1), bf16) and resident in HBM before timing.
+
+value = denoising-call query tokens (50 * B*l*S per step) / wall time of the
+whole step (the cache-writing pass is timed but its tokens are not counted).
+
+Also reported: per-kernel average duration from HIP events on the launch
+stream, the dominant kernel's roofline fraction, the batched 32x32-latent
+case (B=8, 1024 tokens) whose temporal working set (1.5 GB) exceeds the
+256 MB Infinity Cache, and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-large]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention tokens/sec per denoise step; temporal HBM GB/s, spatial MFMA util %"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
+T_DENOISE = 50
+
+AR_STEP = dict(name="ar_step_s256", B=1, H=16, d=72, S=256, l=8, p_max=25, p_spatial=3, tpe_len=33)
+LARGE = dict(name="large_b8_s1024", B=8, H=16, d=72, S=1024, l=8, p_max=25, p_spatial=3, tpe_len=33)
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work per launch
+# ----------------------------------------------------------------------------
+def temporal_bytes(sh, n, p_k, eb=2):
+    C = sh["H"] * sh["d"]
+    tok = sh["B"] * sh["S"] * C * eb
+    return 2 * n * tok + 2 * p_k * tok + 2 * n * tok      # Q + O, cached K/V, new K/V
+
+
+def temporal_flops(sh, n, p_k):
+    rows = sh["B"] * sh["S"] * sh["H"]
+    return rows * sum(p_k + i + 1 for i in range(n)) * 4 * sh["d"]
+
+
+def spatial_flops(sh, n, n_prefix):
+    S = sh["S"]
+    return sh["B"] * n * sh["H"] * 4 * S * (n_prefix + 1) * S * sh["d"]
+
+
+def spatial_bytes(sh, n, n_prefix, eb=2):
+    C = sh["H"] * sh["d"]
+    tok = sh["B"] * sh["S"] * C * eb
+    return 4 * n * tok + 2 * n_prefix * tok                # Q, O, own K, V; prefix K/V read once
+
+
+def write_bytes(sh, n, eb=2):
+    C = sh["H"] * sh["d"]
+    tok = sh["B"] * sh["S"] * C * eb
+    return 2 * (2 * n * tok + 2 * min(n, sh["p_spatial"]) * tok)   # read + write of K/V copies
+
+
+# ----------------------------------------------------------------------------
+def _randn(shape, gen, dtype):
+    import torch
+    return torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(dtype)
+
+
+class Workload:
+    """Device buffers and a cache filled to P_max for one shape."""
+
+    def __init__(self, sh, n_sets, seed):
+        import torch
+        from causal_kv_cache_amd import ca2
+        self.sh = sh
+        self.cache = ca2.Cache(sh["B"], sh["H"], sh["d"], sh["S"], sh["l"], sh["p_max"],
+                               sh["p_spatial"], sh["tpe_len"], "bf16")
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(seed)
+        bf = torch.bfloat16
+        B, l, S, H, d = sh["B"], sh["l"], sh["S"], sh["H"], sh["d"]
+        chunk = (B, l, S, H, d)
+        # fill the queue: conditioning frame, then whole chunks, to P_max frames
+        frames = 0
+        while frames < sh["p_max"]:
+            w = 1 if frames == 0 else l
+            t = [_randn((B, w, S, H, d), gen, bf) for _ in range(4)]
+            self.cache.ca2_cache_write(*t)
+            frames += w
+        self.sets = [tuple(_randn(chunk, gen, bf) for _ in range(3)) for _ in range(n_sets)]
+        self.clean = tuple(_randn(chunk, gen, bf) for _ in range(5))   # qc, kt, vt, ks, vs
+        self.out_t = torch.empty(chunk, dtype=bf, device="cuda")
+        self.out_s = torch.empty(chunk, dtype=bf, device="cuda")
+        torch.cuda.synchronize()
+
+    def denoise(self, i):
+        q, k, v = self.sets[i % len(self.sets)]
+        self.cache.ca2_spatial_attn(q, k, v, self.out_s)
+        self.cache.ca2_temporal_attn(q, k, v, self.out_t)
+
+    def write_pass(self):
+        from causal_kv_cache_amd import ca2
+        qc, kt, vt, ks, vs = self.clean
+        self.cache.ca2_tpe_index(self.sh["l"])
+        self.cache.ca2_temporal_attn(qc, kt, vt, self.out_t)
+        self.cache.ca2_spatial_attn(qc, ks, vs, self.out_s, mode=ca2.CA2_SPATIAL_SELF)
+        self.cache.ca2_cache_write(kt, vt, ks, vs)
+
+    def ar_step(self):
+        for t in range(T_DENOISE):
+            self.denoise(t)
+        self.write_pass()
+
+
+def time_launches(fn, reps):
+    """Average duration of `fn` over `reps` back-to-back launches, from HIP
+    events recorded on the current (launch) stream."""
+    import torch
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps     # microseconds
+
+
+def kernel_table(w: Workload, reps: int):
+    """Per-kernel average launch duration and roofline numbers for one workload."""
+    from causal_kv_cache_amd import ca2
+    sh = w.sh
+    n, pk, ps = sh["l"], sh["p_max"], sh["p_spatial"]
+    c = w.cache
+    sets = w.sets
+    idx = [0]
+
+    def nxt():
+        idx[0] += 1
+        return sets[idx[0] % len(sets)]
+
+    def k_spatial():
+        q, k, v = nxt()
+        c.ca2_spatial_attn(q, k, v, w.out_s)
+
+    def k_temporal():
+        q, k, v = nxt()
+        c.ca2_temporal_attn(q, k, v, w.out_t)
+
+    def k_spatial_self():
+        qc, kt, vt, ks, vs = w.clean
+        c.ca2_spatial_attn(qc, ks, vs, w.out_s, mode=ca2.CA2_SPATIAL_SELF)
+
+    rows = {}
+    us = time_launches(k_spatial, reps)
+    fl = spatial_flops(sh, n, ps)
+    rows["spatial_attn_prefix"] = dict(us=us, flops=fl, bytes=spatial_bytes(sh, n, ps), bound="mfma",
+                                       achieved=fl / us / 1e6, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s")
+    us = time_launches(k_temporal, reps)
+    by = temporal_bytes(sh, n, pk)
+    rows["temporal_attn"] = dict(us=us, flops=temporal_flops(sh, n, pk), bytes=by, bound="hbm",
+                                 achieved=by / us / 1e3, peak=HBM_PEAK_GBS, unit="GB/s")
+    us = time_launches(k_spatial_self, max(4, reps // 4))
+    fl = spatial_flops(sh, n, 0)
+    rows["spatial_attn_self"] = dict(us=us, flops=fl, bytes=spatial_bytes(sh, n, 0), bound="mfma",
+                                     achieved=fl / us / 1e6, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s")
+    for r in rows.values():
+        r["frac"] = r["achieved"] / r["peak"]
+    return rows
+
+
+def _source_hash(name):
+    p = os.path.join(ROOT, "causal_kv_cache_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_key):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
+    or None when missing or when the kernel source changed since they were taken."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    e = t.get(kernel_key)
+    if not e:
+        return None
+    if e.get("source_sha256_16") != _source_hash(e["source"]):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(budget_s: float):
+    """The oracle, as it stands, on the same workload shape: whole denoising
+    calls (temporal + prefix spatial attention, float64) until `budget_s`."""
+    import numpy as np
+    import synth
+    from oracle import RolloutOracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info()}))
+    except Exception:
+        threads, blas = len(os.sched_getaffinity(0)), "?"
+    sh = dict(synth.WORKLOADS["ar_step_s256"])
+    o = RolloutOracle(sh, 1)
+    for wsz in (1, 8, 8, 8):
+        o.write(o.next_frames(wsz))
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        o.denoise_outputs(4, 50 - calls % 50)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 50:
+            break
+    tokens = calls * sh["B"] * sh["l"] * sh["S"]
+    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{calls} whole denoising calls (temporal + prefix spatial attention, float64 "
+                      f"numpy, BLAS {blas}) at the 256-token shape with the queue full, "
+                      f"{el:.1f} s; cache-writing pass not included",
+            "seconds": el}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--kernel-reps", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-large", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from causal_kv_cache_amd import ca2
+    ca2.load()
+    torch.cuda.set_device(0)
+
+    w = Workload(AR_STEP, T_DENOISE, seed=1234)
+    for _ in range(args.warmup):
+        w.ar_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        w.ar_step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    tokens = args.steps * T_DENOISE * AR_STEP["B"] * AR_STEP["l"] * AR_STEP["S"]
+    value = tokens / wall
+
+    kt = kernel_table(w, args.kernel_reps)
+    # dominant kernel of the step: largest total time per step
+    per_step = {"spatial_attn_prefix": T_DENOISE * kt["spatial_attn_prefix"]["us"],
+                "temporal_attn": T_DENOISE * kt["temporal_attn"]["us"],
+                "spatial_attn_self": kt["spatial_attn_self"]["us"]}
+    dom = max(per_step, key=per_step.get)
+    d = kt[dom]
+    src = "spatial_attn.hip" if dom.startswith("spatial") else "temporal_attn.hip"
+    roofline = {"kernel": dom, "bound": d["bound"], "achieved": round(d["achieved"], 3), "peak": d["peak"],
+                "unit": d["unit"], "frac": round(d["frac"], 4),
+                "traffic": traffic_for(f"{dom}@{AR_STEP['name']}"),
+                "per_launch": {"flops": d["flops"], "bytes": d["bytes"], "avg_us": round(d["us"], 3)},
+                "source": src}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": AR_STEP["name"], "batch": 1, "heads": 16, "head_dim": 72, "tokens": 256,
+                   "chunk": 8, "p_max": 25, "p_k": 25, "p_spatial": 3, "denoise_calls_per_step": T_DENOISE},
+        "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r.items()}
+                    for k, r in kt.items()},
+    }
+    del w
+    torch.cuda.empty_cache()
+
+    if not args.no_large:
+        wl = Workload(LARGE, 2, seed=99)
+        kl = kernel_table(wl, max(10, args.kernel_reps // 10))
+        result["large"] = {"workload": LARGE["name"],
+                           "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                                           for kk, vv in r.items()} for k, r in kl.items()},
+                           "temporal_traffic": traffic_for(f"temporal_attn@{LARGE['name']}"),
+                           "spatial_traffic": traffic_for(f"spatial_attn_prefix@{LARGE['name']}")}
+        del wl
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        cb = cpu_baseline(args.cpu_seconds)
+        cb.pop("seconds", None)
+        cb["value"] = round(cb["value"], 2)
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,7 +17,7 @@ constexpr int kCopyUnroll = 4;
 __global__ __launch_bounds__(kCopyThreads) void copy_frames_kernel(CopyArgs a) {
   // Read the job through the kernel-argument segment (uniform scalar loads);
   // indexing the by-value struct with blockIdx.y would copy it to LDS.
-  const CopyArgs* args = reinterpret_cast<const CopyArgs*>(__builtin_amdgcn_kernarg_segment_ptr());
+  const CopyArgs* args = (const CopyArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   const CopyJob j = args->job[blockIdx.y];
   const int b = blockIdx.z;
   const uint4* __restrict__ src = reinterpret_cast<const uint4*>(

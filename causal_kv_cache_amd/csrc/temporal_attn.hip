@@ -244,6 +244,264 @@ __global__ __launch_bounds__(64 * kWaves) void temporal_attn_kernel(TemporalArgs
   }
 }
 
+// ----------------------------------------------------------------------------
+// bf16 kernel: dimension-split rows, K/V streamed from HBM into registers
+// ----------------------------------------------------------------------------
+// A row (b, s, h) is served by 4*QH lanes: 4 dimension groups x QH query
+// groups of 4 queries. Lane g of a quad holds dims {chunks g, g+4, ...} of the
+// row (16-byte pieces) plus dword g of a leftover chunk (d = 72: 2 chunks + 1
+// dword = 18 dims), so every load is aligned and the quad covers the row.
+// q.k is a v_dot2_f32_bf16 partial sum reduced across the quad with two DPP
+// adds; the softmax statistics and the accumulators for the lane's dims stay
+// in registers. The next key's K/V slice is loaded while the current key is
+// processed. The running maximum is only raised when a score exceeds it by
+// more than 2^8 (base-2 units), so the accumulators are rescaled a handful of
+// times per row instead of once per key.
+// When rows are few, the key range is split over up to 4 wavefronts of a
+// workgroup and the partial results are merged through LDS.
+
+template <int D>
+struct DsGeom {
+  static constexpr int C16 = D * 2 / 16;     // 16-byte chunks per row
+  static constexpr int FULL = C16 / 4;       // whole chunks per lane
+  static constexpr int REM = C16 % 4;        // leftover chunks, one dword per lane each
+  static constexpr int DW = FULL * 4 + REM;  // dwords (bf16 pairs) per lane
+  static constexpr int DPL = 2 * DW;         // dims per lane
+  static_assert((D * 2) % 16 == 0, "row must be whole 16-byte chunks");
+};
+
+template <int D>
+struct Slice {
+  uint32_t w[DsGeom<D>::DW];
+};
+
+template <int D>
+__device__ __forceinline__ void load_slice(Slice<D>& s, const unsigned char* row, int g) {
+  using G = DsGeom<D>;
+#pragma unroll
+  for (int c = 0; c < G::FULL; ++c) {
+    const uint4 u = *reinterpret_cast<const uint4*>(row + 16 * (g + 4 * c));
+    s.w[4 * c + 0] = u.x; s.w[4 * c + 1] = u.y; s.w[4 * c + 2] = u.z; s.w[4 * c + 3] = u.w;
+  }
+#pragma unroll
+  for (int r = 0; r < G::REM; ++r)
+    s.w[4 * G::FULL + r] = *reinterpret_cast<const uint32_t*>(row + 16 * (4 * G::FULL + r) + 4 * g);
+}
+
+template <int D>
+__device__ __forceinline__ void store_slice(unsigned char* row, int g, const float* v) {
+  using G = DsGeom<D>;
+#pragma unroll
+  for (int c = 0; c < G::FULL; ++c) {
+    uint4 u;
+    u.x = pack_bf16x2(v[8 * c + 0], v[8 * c + 1]);
+    u.y = pack_bf16x2(v[8 * c + 2], v[8 * c + 3]);
+    u.z = pack_bf16x2(v[8 * c + 4], v[8 * c + 5]);
+    u.w = pack_bf16x2(v[8 * c + 6], v[8 * c + 7]);
+    *reinterpret_cast<uint4*>(row + 16 * (g + 4 * c)) = u;
+  }
+#pragma unroll
+  for (int r = 0; r < G::REM; ++r)
+    *reinterpret_cast<uint32_t*>(row + 16 * (4 * G::FULL + r) + 4 * g) =
+        pack_bf16x2(v[8 * G::FULL + 2 * r], v[8 * G::FULL + 2 * r + 1]);
+}
+
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+  return x;
+}
+
+constexpr float kNoMax = -1.0e30f;   // running max before any visible key (finite: exp2 gives 0)
+constexpr float kLazy = 8.0f;        // raise the running max only past this margin (base 2)
+constexpr int kQPL = 4;              // queries per lane
+
+template <int D, int QH>
+__global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, int splits) {
+  using G = DsGeom<D>;
+  constexpr int DW = G::DW, DPL = G::DPL;
+  constexpr int LPR = 4 * QH;          // lanes per row
+  constexpr int ROWS = 64 / LPR;       // rows per wavefront
+  extern __shared__ float merge_lds[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane & 3;                          // dimension group
+  const int qg = (lane >> 2) % QH;                 // query group
+  const int ri = lane / LPR;
+  const int row = blockIdx.x * ROWS + ri;
+  const bool row_ok = row < a.rows_total;
+  const int rpb = a.rows_per_batch;
+  const int b = row_ok ? row / rpb : 0;
+  const int rr = row_ok ? row % rpb : 0;
+  const int64_t row_bytes = (int64_t)rr * D * 2;
+  const int64_t frame_bytes = (int64_t)rpb * D * 2;
+
+  const unsigned char* qb = static_cast<const unsigned char*>(a.q);
+  const unsigned char* knb = static_cast<const unsigned char*>(a.k_new);
+  const unsigned char* vnb = static_cast<const unsigned char*>(a.v_new);
+  const unsigned char* rkb = static_cast<const unsigned char*>(a.ring_k);
+  const unsigned char* rvb = static_cast<const unsigned char*>(a.ring_v);
+
+  // queries of this lane: frames qg*4 .. qg*4+3 (dims of this lane only)
+  Slice<D> qs[kQPL];
+  bool qok[kQPL];
+  int last_key[kQPL];
+#pragma unroll
+  for (int qq = 0; qq < kQPL; ++qq) {
+    const int qi = qg * kQPL + qq;
+    qok[qq] = row_ok && qi < a.n;
+    last_key[qq] = qok[qq] ? a.p_k + qi : -1;
+    if (qok[qq]) {
+      load_slice<D>(qs[qq], qb + ((int64_t)b * a.n + qi) * frame_bytes + row_bytes, g);
+    } else {
+#pragma unroll
+      for (int w = 0; w < DW; ++w) qs[qq].w[w] = 0u;
+    }
+  }
+
+  // key range of this wavefront
+  const int k_total = a.p_k + a.n;
+  const int per = (k_total + splits - 1) / splits;
+  const int kb = wave * per;
+  const int ke = min(k_total, kb + per);
+
+  auto key_row = [&](int j, const unsigned char* ring, const unsigned char* fresh) -> const unsigned char* {
+    if (j < a.p_k) {
+      int slot = a.head + j;
+      if (slot >= a.p_max) slot -= a.p_max;
+      return ring + ((int64_t)b * a.p_max + slot) * frame_bytes + row_bytes;
+    }
+    return fresh + ((int64_t)b * a.n + (j - a.p_k)) * frame_bytes + row_bytes;
+  };
+
+  float m[kQPL], l[kQPL], acc[kQPL][DPL];
+#pragma unroll
+  for (int qq = 0; qq < kQPL; ++qq) {
+    m[qq] = kNoMax;
+    l[qq] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[qq][e] = 0.f;
+  }
+
+  Slice<D> kc, vc, kn, vn;
+  if (row_ok && kb < ke) {
+    load_slice<D>(kc, key_row(kb, rkb, knb), g);
+    load_slice<D>(vc, key_row(kb, rvb, vnb), g);
+  }
+  for (int j = kb; j < ke; ++j) {
+    if (row_ok && j + 1 < ke) {
+      load_slice<D>(kn, key_row(j + 1, rkb, knb), g);
+      load_slice<D>(vn, key_row(j + 1, rvb, vnb), g);
+    }
+    // scores of the lane's queries against key j
+    float x[kQPL];
+    bool raise = false;
+#pragma unroll
+    for (int qq = 0; qq < kQPL; ++qq) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < DW; ++w)
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, qs[qq].w[w]),
+                                            __builtin_bit_cast(bf16x2v, kc.w[w]), s, false);
+      s = quad_sum(s);
+      x[qq] = (j <= last_key[qq]) ? s * a.scale_log2e : -INFINITY;
+      raise |= x[qq] > m[qq] + kLazy;
+    }
+    if (raise) {
+#pragma unroll
+      for (int qq = 0; qq < kQPL; ++qq) {
+        const float mn = fmaxf(m[qq], x[qq]);
+        const float corr = fast_exp2(m[qq] - mn);
+        m[qq] = mn;
+        l[qq] *= corr;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[qq][e] *= corr;
+      }
+    }
+    float v[DPL];
+#pragma unroll
+    for (int w = 0; w < DW; ++w) {
+      v[2 * w] = bf16_lo(vc.w[w]);
+      v[2 * w + 1] = bf16_hi(vc.w[w]);
+    }
+#pragma unroll
+    for (int qq = 0; qq < kQPL; ++qq) {
+      const float p = fast_exp2(x[qq] - m[qq]);   // 0 for hidden keys
+      l[qq] += p;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[qq][e] = fmaf(p, v[e], acc[qq][e]);
+    }
+    kc = kn;
+    vc = vn;
+  }
+
+  // merge the wavefronts of a split key range
+  if (splits > 1) {
+    constexpr int PER_LANE = kQPL * (DPL + 2);
+    if (wave > 0) {
+      float* dst = merge_lds + (wave - 1) * 64 * PER_LANE + lane;
+#pragma unroll
+      for (int qq = 0; qq < kQPL; ++qq) {
+        dst[(qq * (DPL + 2)) * 64] = m[qq];
+        dst[(qq * (DPL + 2) + 1) * 64] = l[qq];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) dst[(qq * (DPL + 2) + 2 + e) * 64] = acc[qq][e];
+      }
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    for (int w = 1; w < splits; ++w) {
+      const float* src = merge_lds + (w - 1) * 64 * PER_LANE + lane;
+#pragma unroll
+      for (int qq = 0; qq < kQPL; ++qq) {
+        const float mw = src[(qq * (DPL + 2)) * 64];
+        const float mn = fmaxf(m[qq], mw);
+        const float s0 = fast_exp2(m[qq] - mn);
+        const float s1 = fast_exp2(mw - mn);
+        m[qq] = mn;
+        l[qq] = l[qq] * s0 + src[(qq * (DPL + 2) + 1) * 64] * s1;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+          acc[qq][e] = acc[qq][e] * s0 + src[(qq * (DPL + 2) + 2 + e) * 64] * s1;
+      }
+    }
+  }
+
+  unsigned char* ob = static_cast<unsigned char*>(a.out);
+#pragma unroll
+  for (int qq = 0; qq < kQPL; ++qq) {
+    if (!qok[qq]) continue;
+    const int qi = qg * kQPL + qq;
+    const float inv = 1.f / l[qq];
+    float o[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] = acc[qq][e] * inv;
+    store_slice<D>(ob + ((int64_t)b * a.n + qi) * frame_bytes + row_bytes, g, o);
+  }
+}
+
+template <int D, int QH>
+hipError_t launch_ds_q(const TemporalArgs& a, hipStream_t s) {
+  constexpr int ROWS = 64 / (4 * QH);
+  const int groups = (a.rows_total + ROWS - 1) / ROWS;
+  // split the key range when there are too few row groups to fill the chip
+  int splits = (2048 + groups - 1) / groups;
+  splits = splits < 1 ? 1 : splits > 4 ? 4 : splits;
+  const int k_total = a.p_k + a.n;
+  if (splits > k_total) splits = k_total;
+  const size_t lds = splits > 1 ? (size_t)(splits - 1) * 64 * kQPL * (DsGeom<D>::DPL + 2) * sizeof(float) : 0;
+  hipLaunchKernelGGL((temporal_attn_ds_kernel<D, QH>), dim3(groups), dim3(64 * splits), lds, s, a, splits);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_ds(const TemporalArgs& a, hipStream_t s) {
+  if (a.n <= 4) return launch_ds_q<D, 1>(a, s);
+  if (a.n <= 8) return launch_ds_q<D, 2>(a, s);
+  return launch_ds_q<D, 4>(a, s);
+}
+
 template <typename T, int D>
 hipError_t launch_td(const TemporalArgs& a, hipStream_t s) {
   const int ql = a.n <= 4 ? 4 : a.n <= 8 ? 8 : 16;
@@ -276,9 +534,9 @@ hipError_t launch_temporal(int dtype, int d, const TemporalArgs& a, hipStream_t 
     }
   } else if (dtype == 1) {
     switch (d) {
-      case 64: return launch_td<bf16_t, 64>(a, s);
-      case 72: return launch_td<bf16_t, 72>(a, s);
-      case 128: return launch_td<bf16_t, 128>(a, s);
+      case 64: return launch_ds<64>(a, s);
+      case 72: return launch_ds<72>(a, s);
+      case 128: return launch_ds<128>(a, s);
     }
   }
   return hipErrorInvalidValue;
