@@ -84,6 +84,12 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                            "(there is no fallback implementation)")
+    # torch ships its own HIP runtime; load it first so that libca2 binds to the
+    # same libamdhip64 instance instead of initialising a second runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)

@@ -22,15 +22,24 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 
+#include <cstdlib>
+
 namespace ca2 {
 namespace {
 
 // ----------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ----------------------------------------------------------------------------
+// Pipeline: key tiles of 64 keys stream through a 3-stage LDS ring. Each tile
+// is copied HBM -> LDS by global_load_lds_dwordx4 (asynchronous DMA, 16 bytes
+// per lane, no register staging) two tiles ahead of its use; a wavefront waits
+// only for its own copies of the tile it is about to read (s_waitcnt vmcnt),
+// then one barrier per tile publishes it to the workgroup. K and V stay
+// row-major in LDS; the V^T operand of the PV product is read with
+// ds_read_b64_tr_b16, which transposes 16-bit data across each 16-lane group.
 constexpr int kBN = 64;                  // keys per tile
 constexpr int kSW = 4;                   // wavefronts per workgroup
-constexpr int kVtStride = kBN * 2 + 8;   // bytes per V^T row in LDS
+constexpr int kStages = 3;               // LDS ring depth (prefetch distance 2)
 constexpr float kNoMax = -1.0e30f;       // running max before the first tile
 constexpr float kLazy = 8.0f;            // raise the running max only past this margin (base 2)
 
@@ -38,54 +47,98 @@ template <int D>
 struct SCfg {
   static constexpr int KSTEPS = (D + 15) / 16;     // QK^T contraction steps of 16 dims
   static constexpr int DBLK = (D + 31) / 32;       // PV output blocks of 32 dims
-  static constexpr int DP = DBLK * 32;             // V^T rows incl. padding rows
-  static constexpr bool ONES = DP > D;             // padding row D holds 1.0: MFMA row sums
-  static constexpr int CPR = D / 8;                // 16-byte chunks per key row
-  // K row stride in LDS: d*2 bytes, +16 when d*2 is a multiple of 128 so that
-  // 8 consecutive rows start in distinct banks
-  static constexpr int KSTR = D * 2 + ((D * 2) % 128 == 0 ? 16 : 0);
-  static constexpr int K_BYTES = kBN * KSTR + 32;  // + zero pad read by the last k-step
-  static constexpr int VT_BYTES = DP * kVtStride;
-  static constexpr int BUF = K_BYTES + VT_BYTES;   // one stage
-  static constexpr int K_CHUNKS = kBN * CPR;       // 16-byte K pieces per tile
-  static constexpr int K_PER_T = (K_CHUNKS + 64 * kSW - 1) / (64 * kSW);
-  static constexpr int V_UNITS = (kBN / 4) * CPR;  // (4 keys x 8 dims) V pieces per tile
+  static constexpr int DP = DBLK * 32;
+  static constexpr bool ONES = DP > D;             // V row padding holds 1.0 at dim D: MFMA row sums
+  static constexpr int CH = D / 8;                 // 16-byte chunks of data per key row
+  // K row = KSL 16-byte slots. 8 rows read by one ds_read_b128 pass must start
+  // in distinct banks: odd slot counts do that.
+  static constexpr int KSL = CH % 2 ? CH : CH + 1;
+  // V row = VSL slots. The transposing read touches 4 consecutive rows x 32
+  // bytes per 16-lane group: rows must be 8 or 24 dwords apart mod 32.
+  static constexpr int VSL = (CH + 1) % 8 == 2 || (CH + 1) % 8 == 6 ? CH + 1 : (CH + 2) % 8 == 2 || (CH + 2) % 8 == 6 ? CH + 2 : CH + 3;
+  static constexpr int KROW = KSL * 16, VROW = VSL * 16;
+  static constexpr int K_BYTES = kBN * KROW + 32;   // + pad read by the last QK k-step
+  static constexpr int V_OFF = K_BYTES;
+  static constexpr int V_BYTES = kBN * VROW + 64;   // + pad read past the last row
+  static constexpr int STAGE = (K_BYTES + V_BYTES + 15) / 16 * 16;
+  static constexpr int NI = KSL + VSL;              // 64-lane copy instructions per tile
+  static constexpr int MAXI = (NI + kSW - 1) / kSW; // per wavefront
   static_assert(D % 8 == 0, "head_dim must be a multiple of 8");
-  static_assert(V_UNITS <= 64 * kSW, "one V unit per thread");
+  static_assert((VSL * 4) % 32 == 8 || (VSL * 4) % 32 == 24, "V row stride");
+  static_assert(!ONES || VSL > CH, "ones column needs a padding slot");
 };
 
-// max of a lane's value and its partner lane (lane ^ 32)
+// max / sum of a lane's value and its partner lane (lane ^ 32)
 __device__ __forceinline__ float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
                                             __builtin_bit_cast(unsigned, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  return __builtin_fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
-
 __device__ __forceinline__ float sum_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
                                             __builtin_bit_cast(unsigned, x), false, false);
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
+// 16-byte global -> LDS copy for every active lane: lane i writes
+// lds_addr + 16*i (lds_addr is wavefront-uniform, held in M0). The copy has
+// no register result; completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const void* gptr, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
+
+// Block index -> work index such that XCD x (which receives blocks x, x+8,
+// x+16, ...) processes work items [start_x, start_x + count_x) in order.
+__device__ __forceinline__ int xcd_work_index(int block, int nblocks) {
+  constexpr int kXcds = 8;
+  const int q = nblocks / kXcds, r = nblocks % kXcds;
+  const int x = block % kXcds, local = block / kXcds;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
+
 // QB query blocks of 32 per wavefront (32*QB*kSW queries per workgroup).
 template <int D, int QB>
-__global__ __launch_bounds__(64 * kSW) void spatial_attn_mfma_kernel(SpatialArgs a) {
+__global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))) void spatial_attn_mfma_kernel(SpatialArgs a) {
   using C = SCfg<D>;
-  constexpr int KSTEPS = C::KSTEPS, DBLK = C::DBLK, DP = C::DP, CPR = C::CPR, KSTR = C::KSTR;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::BUF];
+  constexpr int KSTEPS = C::KSTEPS, DBLK = C::DBLK, KSL = C::KSL, VSL = C::VSL, CH = C::CH;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * C::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;            // k-half of the MFMA operands
   const int col = lane & 31;             // query column owned by this lane
-  const int head = blockIdx.y % a.heads;
-  const int f = blockIdx.y / a.heads;
-  const int b = blockIdx.z;
   const int S = a.tokens;
+  // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
+  // Give every XCD a contiguous run of work items ordered (b, head, frame,
+  // query block), so the query blocks of one frame and the frames sharing the
+  // same prefix frames read their K/V through the same L2.
+  const int nq = (S + 32 * QB * kSW - 1) / (32 * QB * kSW);
+  const int w = xcd_work_index(blockIdx.x, gridDim.x);
+  const int qblk = w % nq;
+  const int f = (w / nq) % a.n;
+  const int head = (w / (nq * a.n)) % a.heads;
+  const int b = w / (nq * a.n * a.heads);
   const int64_t tok_stride = (int64_t)a.heads * D;           // elements between tokens
   const int64_t own_off = (((int64_t)b * a.n + f) * S) * tok_stride + (int64_t)head * D;
-  const int q_base = blockIdx.x * (32 * QB * kSW) + wave * (32 * QB);
+  const int q_base = qblk * (32 * QB * kSW) + wave * (32 * QB);
 
   // Q^T operands (B of S^T = K Q^T): dims 16s + 8*half .. +7 of each query column
   bf16x8v qop[QB][KSTEPS];
@@ -104,86 +157,65 @@ __global__ __launch_bounds__(64 * kSW) void spatial_attn_mfma_kernel(SpatialArgs
     }
   }
 
-  // padding of both stages: V^T rows D..DP-1 (row D = 1.0 for the row sums)
-  // and the tail of the K tile read by the last k-step
-  for (int st = 0; st < 2; ++st) {
-    unsigned char* vt = smem + st * C::BUF + C::K_BYTES;
-    for (int i = tid; i < (DP - D) * (kVtStride / 4); i += 64 * kSW) {
-      const int r = i / (kVtStride / 4);
-      reinterpret_cast<uint32_t*>(vt + D * kVtStride)[i] = (C::ONES && r == 0) ? 0x3F803F80u : 0u;
+  // LDS init: zero everything, then 1.0 at dim D of every V row (the padding
+  // slot right after the data); copies never touch padding slots.
+  for (int i = tid; i < kStages * C::STAGE / 16; i += 64 * kSW)
+    reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  if constexpr (C::ONES) {
+    for (int i = tid; i < kStages * kBN; i += 64 * kSW) {
+      const int st = i / kBN, row = i % kBN;
+      *reinterpret_cast<uint32_t*>(smem + st * C::STAGE + C::V_OFF + row * C::VROW + CH * 16) = 0x3F80u;
     }
-    if (tid < 8) reinterpret_cast<uint32_t*>(smem + st * C::BUF + kBN * KSTR)[tid] = 0u;
+  }
+  __syncthreads();
+  const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+
+  // copy instructions of this wavefront: j = wave, wave+4, ... < NI
+  // (j < KSL: K slots j*64 .. +63; else V slots (j-KSL)*64 .. +63)
+  const int n_mine = (C::NI - wave + kSW - 1) / kSW;
+  int g_off[C::MAXI], g_row[C::MAXI];
+  bool g_ok[C::MAXI];
+#pragma unroll
+  for (int i = 0; i < C::MAXI; ++i) {
+    const int j = wave + kSW * i;
+    const bool isv = j >= KSL;
+    const int slot = (isv ? j - KSL : j) * 64 + lane;
+    const int row = slot / (isv ? VSL : KSL), c = slot % (isv ? VSL : KSL);
+    g_ok[i] = j < C::NI && c < CH;
+    g_row[i] = row;
+    g_off[i] = row * (int)tok_stride + c * 8;
   }
 
   const int tiles_per_frame = (S + kBN - 1) / kBN;
   const int n_tiles = (1 + a.n_prefix) * tiles_per_frame;
-
-  auto frame_ptrs = [&](int kf, const bf16_t*& kbase, const bf16_t*& vbase) {
-    if (kf == 0) {
-      kbase = static_cast<const bf16_t*>(a.k) + own_off;
-      vbase = static_cast<const bf16_t*>(a.v) + own_off;
-    } else {
-      const int64_t off = (((int64_t)b * a.p_slots + a.prefix_slot[kf - 1]) * S) * tok_stride +
-                          (int64_t)head * D;
-      kbase = static_cast<const bf16_t*>(a.sp_k) + off;
-      vbase = static_cast<const bf16_t*>(a.sp_v) + off;
-    }
-  };
-
-  // register staging of one tile: K pieces and one V unit per thread
-  uint4 kreg[C::K_PER_T];
-  uint4 vreg[4];
-  const int v_unit = tid;                 // (key group kg, dim chunk c)
-  const int v_kg = v_unit / CPR, v_c = v_unit % CPR;
-  auto load_tile = [&](int t) {
+  auto tile_full = [&](int t) { return t < n_tiles && S - (t % tiles_per_frame) * kBN >= kBN; };
+  auto issue_tile = [&](int t) {
     const int kf = t / tiles_per_frame;
     const int t0 = (t % tiles_per_frame) * kBN;
     const int nk = min(kBN, S - t0);
-    const bf16_t* kbase;
-    const bf16_t* vbase;
-    frame_ptrs(kf, kbase, vbase);
-#pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int e = tid + i * 64 * kSW;
-      const int key = e / CPR, c = e % CPR;
-      kreg[i] = make_uint4(0, 0, 0, 0);
-      if (e < C::K_CHUNKS && key < nk)
-        kreg[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(t0 + key) * tok_stride + c * 8);
+    int64_t off;
+    const bf16_t* kb;
+    const bf16_t* vb;
+    if (kf == 0) {
+      off = own_off;
+      kb = static_cast<const bf16_t*>(a.k);
+      vb = static_cast<const bf16_t*>(a.v);
+    } else {
+      off = (((int64_t)b * a.p_slots + a.prefix_slot[kf - 1]) * S) * tok_stride + (int64_t)head * D;
+      kb = static_cast<const bf16_t*>(a.sp_k);
+      vb = static_cast<const bf16_t*>(a.sp_v);
     }
+    off += (int64_t)t0 * tok_stride;
+    const unsigned st = lds_base + (t % kStages) * C::STAGE;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int key = v_kg * 4 + kk;
-      vreg[kk] = make_uint4(0, 0, 0, 0);
-      if (v_unit < C::V_UNITS && key < nk)
-        vreg[kk] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(t0 + key) * tok_stride + v_c * 8);
-    }
-  };
-  auto store_tile = [&](int st) {
-    unsigned char* ks = smem + st * C::BUF;
-    unsigned char* vt = ks + C::K_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int e = tid + i * 64 * kSW;
-      if (e < C::K_CHUNKS) {
-        const int key = e / CPR, c = e % CPR;
-        *reinterpret_cast<uint4*>(ks + key * KSTR + c * 16) = kreg[i];
-      }
-    }
-    if (v_unit < C::V_UNITS) {
-      const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-      const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-      const uint32_t* x2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-      const uint32_t* x3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        uint2 lo, hi;     // dims 8c + 2qd and 8c + 2qd + 1, keys 4kg .. 4kg+3
-        lo.x = __builtin_amdgcn_perm(x1[qd], x0[qd], 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(x3[qd], x2[qd], 0x05040100u);
-        hi.x = __builtin_amdgcn_perm(x1[qd], x0[qd], 0x07060302u);
-        hi.y = __builtin_amdgcn_perm(x3[qd], x2[qd], 0x07060302u);
-        const int dim = v_c * 8 + 2 * qd;
-        *reinterpret_cast<uint2*>(vt + dim * kVtStride + v_kg * 8) = lo;
-        *reinterpret_cast<uint2*>(vt + (dim + 1) * kVtStride + v_kg * 8) = hi;
+    for (int i = 0; i < C::MAXI; ++i) {
+      const int j = wave + kSW * i;
+      if (j < C::NI) {
+        const bool isv = j >= KSL;
+        const unsigned dst = st + (isv ? C::V_OFF + (j - KSL) * 1024 : j * 1024);
+        const bf16_t* src = (isv ? vb : kb) + off + g_off[i];
+        if (g_ok[i] && g_row[i] < nk) dma16(src, __builtin_amdgcn_readfirstlane(dst));
       }
     }
   };
@@ -196,103 +228,103 @@ __global__ __launch_bounds__(64 * kSW) void spatial_attn_mfma_kernel(SpatialArgs
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[qb][i][r] = 0.f;
   float m_run[QB];
-  float l_run[QB];            // explicit row sums (only without the ones row)
+  float l_run[QB];            // explicit row sums (only without the ones column)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { m_run[qb] = kNoMax; l_run[qb] = 0.f; }
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  issue_tile(0);
+  if (n_tiles > 1) issue_tile(1);
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int st = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);       // in flight during this tile's math
-    const unsigned char* ks = smem + st * C::BUF;
-    const unsigned char* vt = ks + C::K_BYTES;
-    const int nk = min(kBN, S - (t % tiles_per_frame) * kBN);
+    // wait for this wavefront's copies of tile t (tile t+1's may stay in
+    // flight when it is a full tile, whose copy count is exact), then publish
+    if (tile_full(t + 1) && tile_full(t)) {
+      if (n_mine == C::MAXI) wait_vmcnt<C::MAXI>(); else wait_vmcnt<C::MAXI - 1>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();                     // also: every wavefront is done with tile t-1
+    if (t + 2 < n_tiles) issue_tile(t + 2);   // into the stage tile t-1 used
 
-    // -- S^T = K Q^T: two key blocks of 32, each query block --
-    f32x16 sc[QB][2];
+    const unsigned char* ks = smem + (t % kStages) * C::STAGE;
+    const unsigned char* vs = ks + C::V_OFF;
+    const int nk = min(kBN, S - (t % tiles_per_frame) * kBN);
+    const f32x16 zero16 = {};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[qb][kb][r] = 0.f;
-      const unsigned char* krow = ks + (kb * 32 + col) * KSTR;
+      // -- S^T = K Q^T for keys kb*32 .. +31 --
+      f32x16 sc[QB];
+      const unsigned char* krow = ks + (kb * 32 + col) * C::KROW;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         const bf16x8v kop = *reinterpret_cast<const bf16x8v*>(krow + (16 * s + 8 * half) * 2);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          sc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[qb][s], sc[qb][kb], 0, 0, 0);
+          sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[qb][s], s == 0 ? zero16 : sc[qb], 0, 0, 0);
       }
-    }
-    // register r of sc[.][kb] holds key kb*32 + 8*(r/4) + 4*half + r%4
-    if (nk < kBN) {
+      // register r of sc[.] holds key kb*32 + 8*(r/4) + 4*half + r%4
+      if (nk < kBN) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key >= nk) sc[qb][kb][r] = -INFINITY;
+            if (key >= nk) sc[qb][r] = -INFINITY;
           }
-    }
-
-    bf16x8v pf[QB][4];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // -- tile max (max3 tree), shared with the partner half --
-      float mx = fmaxf(sc[qb][0][0], sc[qb][0][1]);
-#pragma unroll
-      for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[qb][0][r]), sc[qb][0][r + 1]);
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[qb][1][r]), sc[qb][1][r + 1]);
-      mx = max_halves(mx) * a.scale_log2e;
-      // -- lazy rescale: only when the tile max passes the running max by > 2^8 --
-      if (mx > m_run[qb] + kLazy) {
-        const float corr = fast_exp2(m_run[qb] - mx);
-        m_run[qb] = mx;
-        l_run[qb] *= corr;
-#pragma unroll
-        for (int i = 0; i < DBLK; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[qb][i][r] *= corr;
       }
-      const float mneg = -m_run[qb];
+      bf16x8v pf[QB][2];
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        const int kb = mm >> 1, r0 = 8 * (mm & 1);
-        uint32_t w[4];
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = __builtin_fmaxf(sc[qb][0], sc[qb][1]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(fmaf(sc[qb][kb][r0 + 2 * e], a.scale_log2e, mneg));
-          const float p1 = fast_exp2(fmaf(sc[qb][kb][r0 + 2 * e + 1], a.scale_log2e, mneg));
-          if constexpr (!C::ONES) l_run[qb] += p0 + p1;
-          w[e] = pack_bf16x2(p0, p1);
+        for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[qb][r]), sc[qb][r + 1]);
+        mx = max_halves(mx) * a.scale_log2e;
+        // lazy rescale: only when the max passes the running max by > 2^8
+        if (mx > m_run[qb] + kLazy) {
+          const float corr = fast_exp2(m_run[qb] - mx);
+          m_run[qb] = mx;
+          l_run[qb] *= corr;
+#pragma unroll
+          for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[qb][i][r] *= corr;
         }
-        pf[qb][mm] = __builtin_bit_cast(bf16x8v, make_uint4(w[0], w[1], w[2], w[3]));
+        const float mneg = -m_run[qb];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          uint32_t wv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(fmaf(sc[qb][8 * h2 + 2 * e], a.scale_log2e, mneg));
+            const float p1 = fast_exp2(fmaf(sc[qb][8 * h2 + 2 * e + 1], a.scale_log2e, mneg));
+            if constexpr (!C::ONES) l_run[qb] += p0 + p1;
+            wv[e] = pack_bf16x2(p0, p1);
+          }
+          pf[qb][h2] = __builtin_bit_cast(bf16x8v, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+        }
+      }
+      // -- O^T += V^T P^T over these 32 keys, k-steps of 16 (mm = 2kb + h2).
+      //    Element e of the operands is key 16mm + 4*half + e (+4 for e >= 4).
+      //    Transposing read: lane 16g + j addresses key row 16mm + 4*(g/2) +
+      //    j/4 (+8 for the second read) at dims 32i + 16*(g%2) + 4*(j%4); it
+      //    receives dim 32i + (lane%32) of keys 16mm + 4*(g/2) + 0..3.
+      const int g16 = lane >> 4, j16 = lane & 15;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int mm = 2 * kb + h2;
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i) {
+          const unsigned char* p0 = vs + (16 * mm + 4 * (g16 >> 1) + (j16 >> 2)) * C::VROW +
+                                    (32 * i + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
+          const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+          const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 8 * C::VROW));
+          const bf16x8v vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            acc[qb][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf[qb][h2], acc[qb][i], 0, 0, 0);
+        }
       }
     }
-    // -- O^T += V^T P^T: k-steps of 16 keys; element e of the operands is key
-    //    16*mm + 4*half + e (+4 for e >= 4) --
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-#pragma unroll
-      for (int i = 0; i < DBLK; ++i) {
-        const unsigned char* vrow = vt + (i * 32 + col) * kVtStride;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (16 * mm + 4 * half) * 2);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (16 * mm + 8 + 4 * half) * 2);
-        const bf16x8v vop = __builtin_bit_cast(bf16x8v, make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          acc[qb][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf[qb][mm], acc[qb][i], 0, 0, 0);
-      }
-    }
-    if (t + 1 < n_tiles) store_tile(st ^ 1);   // the other stage was last read in tile t-1
-    __syncthreads();
   }
 
   // -- normalise and write: register r of acc[.][i] is dim 32i + 8(r/4) + 4*half + r%4 --
@@ -300,13 +332,13 @@ __global__ __launch_bounds__(64 * kSW) void spatial_attn_mfma_kernel(SpatialArgs
   for (int qb = 0; qb < QB; ++qb) {
     float l_tot;
     if constexpr (C::ONES) {
-      // row sum = O^T row D (the ones row): register 4*((D%32)/8) + D%4 of
-      // block D/32 in the lanes of half (D%8)/4; the same register of the other
-      // half holds row D+4, an all-zero padding row, so adding the halves gives
+      // row sum = O^T row D (the ones column): register 4*((D%32)/8) + D%4 of
+      // block D/32 in the lanes of half 0; the same register of half 1 holds
+      // row D+4, whose V column is zero padding, so adding the halves gives
       // the sum in every lane
       constexpr int RD = D % 32;
       constexpr int REG = 4 * (RD / 8) + (RD % 4);
-      static_assert(RD % 8 == 0 && D + 4 < DP, "row D+4 must be a zero padding row");
+      static_assert(RD % 8 == 0 && D + 4 < C::DP, "row D+4 must be a zero padding row");
       l_tot = sum_halves(acc[qb][D / 32][REG]);
     } else {
       l_tot = sum_halves(l_run[qb]);
@@ -321,10 +353,10 @@ __global__ __launch_bounds__(64 * kSW) void spatial_attn_mfma_kernel(SpatialArgs
       for (int g = 0; g < 4; ++g) {
         const int dim = 32 * i + 8 * g + 4 * half;
         if (dim < D) {
-          uint2 w;
-          w.x = pack_bf16x2(acc[qb][i][4 * g + 0] * inv, acc[qb][i][4 * g + 1] * inv);
-          w.y = pack_bf16x2(acc[qb][i][4 * g + 2] * inv, acc[qb][i][4 * g + 3] * inv);
-          *reinterpret_cast<uint2*>(op + dim) = w;
+          uint2 wv;
+          wv.x = pack_bf16x2(acc[qb][i][4 * g + 0] * inv, acc[qb][i][4 * g + 1] * inv);
+          wv.y = pack_bf16x2(acc[qb][i][4 * g + 2] * inv, acc[qb][i][4 * g + 3] * inv);
+          *reinterpret_cast<uint2*>(op + dim) = wv;
         }
       }
   }
@@ -404,16 +436,23 @@ __global__ __launch_bounds__(64) void spatial_attn_f32_kernel(SpatialArgs a) {
 template <int D, int QB>
 hipError_t launch_mfma_qb(const SpatialArgs& a, hipStream_t s) {
   constexpr int BM = 32 * QB * kSW;
-  const dim3 grid((a.tokens + BM - 1) / BM, a.n * a.heads, a.batch);
-  hipLaunchKernelGGL((spatial_attn_mfma_kernel<D, QB>), grid, dim3(64 * kSW), 0, s, a);
+  const int64_t nwg = (int64_t)((a.tokens + BM - 1) / BM) * a.n * a.heads * a.batch;
+  if (nwg > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((spatial_attn_mfma_kernel<D, QB>), dim3((unsigned)nwg), dim3(64 * kSW), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_mfma(const SpatialArgs& a, hipStream_t s) {
-  // two query blocks per wavefront when that still gives >= 2 workgroups per CU
+  // Two query blocks of 32 per wavefront halve the LDS operand traffic per
+  // MFMA; used when the grid still gives >= 4 workgroups per CU (and the
+  // registers fit: d <= 72). Both variants run two wavefronts per SIMD.
   const int64_t wg2 = (int64_t)((a.tokens + 255) / 256) * a.n * a.heads * a.batch;
-  if (wg2 >= 512) return launch_mfma_qb<D, 2>(a, s);
+  const char* force = getenv("CA2_SPATIAL_QB");
+  const bool qb2 = force ? force[0] == '2' : (D <= 72 && wg2 >= 1024);
+  if constexpr (D <= 72) {
+    if (qb2) return launch_mfma_qb<D, 2>(a, s);
+  }
   return launch_mfma_qb<D, 1>(a, s);
 }
 
