@@ -17,6 +17,8 @@ case (B=8, 1024 tokens) whose temporal working set (1.5 GB) exceeds the
 256 MB Infinity Cache, and the CPU oracle timed on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-large]
+       python bench.py --kernel {spatial_prefix,temporal,spatial_self,cache_write,qkv_proj}
+                       --workload {ar_step_s256,large_b8_s1024,write_b4} --reps R   (one kernel, for profilers)
 """
 from __future__ import annotations
 
@@ -38,6 +40,9 @@ T_DENOISE = 50
 
 AR_STEP = dict(name="ar_step_s256", B=1, H=16, d=72, S=256, l=8, p_max=25, p_spatial=3, tpe_len=33)
 LARGE = dict(name="large_b8_s1024", B=8, H=16, d=72, S=1024, l=8, p_max=25, p_spatial=3, tpe_len=33)
+WRITE = dict(name="write_b4", B=4, H=16, d=72, S=256, l=8, p_max=41, p_spatial=3, tpe_len=49)
+WORKLOADS = {w["name"]: w for w in (AR_STEP, LARGE, WRITE)}
+KERNELS = ("spatial_prefix", "temporal", "spatial_self", "cache_write", "qkv_proj")
 
 
 # ----------------------------------------------------------------------------
@@ -181,26 +186,78 @@ def kernel_table(w: Workload, reps: int):
     return rows
 
 
-def _source_hash(name):
-    p = os.path.join(ROOT, "causal_kv_cache_amd", "csrc", name)
+SOURCES = {"spatial_prefix": "spatial_attn.hip", "spatial_self": "spatial_attn.hip",
+           "temporal": "temporal_attn.hip", "cache_write": "cache_write.hip", "qkv_proj": "qkv_proj.hip"}
+
+
+def source_hash(kernel):
+    p = os.path.join(ROOT, "causal_kv_cache_amd", "csrc", SOURCES[kernel])
     with open(p, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_for(kernel_key):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
-    or None when missing or when the kernel source changed since they were taken."""
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs (profiles/traffic.json, already scaled by the copy-kernel calibration),
+    or None when missing or when the kernel source changed since."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    e = t.get(kernel_key)
-    if not e:
+    e = t.get("kernels", {}).get(f"{kernel}@{workload}")
+    if not e or e.get("source_sha256_16") != source_hash(kernel):
         return None
-    if e.get("source_sha256_16") != _source_hash(e["source"]):
-        return None
-    return e.get("bytes_per_launch")
+    return e.get("hbm_bytes_per_launch")
+
+
+def write_case(reps):
+    """Cache-writing stage at write_b4: QKV projection of the clean chunk
+    (B*l*S x 1152 -> 3 x 1152) and the cache write of its K/V."""
+    import torch
+    from causal_kv_cache_amd import ca2
+    sh = WRITE
+    B, l, S, H, d = sh["B"], sh["l"], sh["S"], sh["H"], sh["d"]
+    m, c = B * l * S, H * d
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    x = _randn((m, c), gen, torch.bfloat16)
+    wgt = (torch.randn((3 * c, c), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+    q, k, v = (torch.empty((m, c), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    w = Workload(sh, 1, seed=8)
+    kk, vv = k.view(B, l, S, H, d), v.view(B, l, S, H, d)
+    us_p = time_launches(lambda: ca2.ca2_qkv_proj(x, wgt, q, k, v), reps)
+    us_w = time_launches(lambda: w.cache.ca2_cache_write(kk, vv, kk, vv), reps)
+    fl = 2 * m * c * 3 * c
+    wb = write_bytes(sh, l)
+    shared = w.cache.ca2_cache_info_get()["bytes_resident"]
+    return {"workload": sh["name"],
+            "qkv_proj": {"us": round(us_p, 3), "flops": fl, "achieved_tflops": round(fl / us_p / 1e6, 2),
+                         "frac_mfma": round(fl / us_p / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": traffic_for("qkv_proj", sh["name"])},
+            "cache_write": {"us": round(us_w, 3), "bytes": wb, "achieved_gbs": round(wb / us_w / 1e3, 1),
+                            "frac_hbm": round(wb / us_w / 1e3 / HBM_PEAK_GBS, 4),
+                            "traffic": traffic_for("cache_write", sh["name"])},
+            "bytes_resident": {"shared_cache": shared, "per_timestep_copies_T50": 50 * shared}}
+
+
+def kernel_mode(kernel, workload, reps):
+    """Launch one kernel of one workload `reps` times (for profilers)."""
+    import torch
+    from causal_kv_cache_amd import ca2
+    sh = WORKLOADS[workload]
+    if kernel == "qkv_proj":
+        r = write_case(reps)
+        return {"kernel": kernel, "workload": workload, **r["qkv_proj"]}
+    w = Workload(sh, 2, seed=11)
+    q, k, v = w.sets[0]
+    qc, kt, vt, ks, vs = w.clean
+    fn = {"spatial_prefix": lambda: w.cache.ca2_spatial_attn(q, k, v, w.out_s),
+          "spatial_self": lambda: w.cache.ca2_spatial_attn(qc, ks, vs, w.out_s, mode=ca2.CA2_SPATIAL_SELF),
+          "temporal": lambda: w.cache.ca2_temporal_attn(q, k, v, w.out_t),
+          "cache_write": lambda: w.cache.ca2_cache_write(kt, vt, ks, vs)}[kernel]
+    us = time_launches(fn, reps)
+    return {"kernel": kernel, "workload": workload, "reps": reps, "avg_us": round(us, 3)}
 
 
 def cpu_baseline(budget_s: float):
@@ -244,6 +301,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-large", action="store_true")
+    ap.add_argument("--kernel", choices=KERNELS, help="only launch this kernel (profiling mode)")
+    ap.add_argument("--workload", choices=tuple(WORKLOADS), default=AR_STEP["name"])
+    ap.add_argument("--reps", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -254,6 +314,9 @@ def main():
     from causal_kv_cache_amd import ca2
     ca2.load()
     torch.cuda.set_device(0)
+    if args.kernel:
+        print(json.dumps(kernel_mode(args.kernel, args.workload, args.reps)), flush=True)
+        return
 
     w = Workload(AR_STEP, T_DENOISE, seed=1234)
     for _ in range(args.warmup):
@@ -278,12 +341,13 @@ def main():
                 "spatial_attn_self": kt["spatial_attn_self"]["us"]}
     dom = max(per_step, key=per_step.get)
     d = kt[dom]
-    src = "spatial_attn.hip" if dom.startswith("spatial") else "temporal_attn.hip"
-    roofline = {"kernel": dom, "bound": d["bound"], "achieved": round(d["achieved"], 3), "peak": d["peak"],
+    kname = {"spatial_attn_prefix": "spatial_prefix", "temporal_attn": "temporal",
+             "spatial_attn_self": "spatial_self"}[dom]
+    roofline = {"bound": d["bound"], "achieved": round(d["achieved"], 3), "peak": d["peak"],
                 "unit": d["unit"], "frac": round(d["frac"], 4),
-                "traffic": traffic_for(f"{dom}@{AR_STEP['name']}"),
-                "per_launch": {"flops": d["flops"], "bytes": d["bytes"], "avg_us": round(d["us"], 3)},
-                "source": src}
+                "traffic": traffic_for(kname, AR_STEP["name"]),
+                "kernel": dom,
+                "per_launch": {"flops": d["flops"], "bytes": d["bytes"], "avg_us": round(d["us"], 3)}}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -306,9 +370,11 @@ def main():
         result["large"] = {"workload": LARGE["name"],
                            "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                                            for kk, vv in r.items()} for k, r in kl.items()},
-                           "temporal_traffic": traffic_for(f"temporal_attn@{LARGE['name']}"),
-                           "spatial_traffic": traffic_for(f"spatial_attn_prefix@{LARGE['name']}")}
+                           "temporal_traffic": traffic_for("temporal", LARGE["name"]),
+                           "spatial_traffic": traffic_for("spatial_prefix", LARGE["name"])}
         del wl
+        torch.cuda.empty_cache()
+        result["write_case"] = write_case(max(10, args.kernel_reps // 10))
         torch.cuda.empty_cache()
 
     if not args.no_cpu:
