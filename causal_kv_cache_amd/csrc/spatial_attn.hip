@@ -38,12 +38,10 @@ namespace {
 // row-major in LDS; the V^T operand of the PV product is read with
 // ds_read_b64_tr_b16, which transposes 16-bit data across each 16-lane group.
 constexpr int kBN = 64;                  // keys per tile
-constexpr int kSW = 4;                   // wavefronts per workgroup
-constexpr int kStages = 3;               // LDS ring depth (prefetch distance 2)
 constexpr float kNoMax = -1.0e30f;       // running max before the first tile
 constexpr float kLazy = 8.0f;            // raise the running max only past this margin (base 2)
 
-template <int D>
+template <int D, int kSW>
 struct SCfg {
   static constexpr int KSTEPS = (D + 15) / 16;     // QK^T contraction steps of 16 dims
   static constexpr int DBLK = (D + 31) / 32;       // PV output blocks of 32 dims
@@ -113,16 +111,18 @@ __device__ __forceinline__ int xcd_work_index(int block, int nblocks) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
 }
 
-// QB query blocks of 32 per wavefront (32*QB*kSW queries per workgroup).
-template <int D, int QB>
+// QB query blocks of 32 per wavefront, kSW wavefronts per workgroup (32*QB*kSW
+// queries), kStages-deep LDS ring (prefetch distance kStages-1).
+template <int D, int QB, int kSW, int kStages>
 __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))) void spatial_attn_mfma_kernel(SpatialArgs a) {
-  using C = SCfg<D>;
+  using C = SCfg<D, kSW>;
+  static_assert(kStages == 2 || kStages == 3, "ring depth");
   constexpr int KSTEPS = C::KSTEPS, DBLK = C::DBLK, KSL = C::KSL, VSL = C::VSL, CH = C::CH;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * C::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps per-wave state scalar
   const int half = lane >> 5;            // k-half of the MFMA operands
   const int col = lane & 31;             // query column owned by this lane
   const int S = a.tokens;
@@ -157,67 +157,77 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
   }
 
-  // LDS init: zero everything, then 1.0 at dim D of every V row (the padding
-  // slot right after the data); copies never touch padding slots.
+  // The Q operands must be complete before the copy stream starts: vmcnt also
+  // counts the copies, so a wait for Q inside the loop would drain them too.
+  wait_vmcnt<0>();
+
+  // LDS init: zero everything once (rows past a partial tile stay finite)
   for (int i = tid; i < kStages * C::STAGE / 16; i += 64 * kSW)
     reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
-  if constexpr (C::ONES) {
-    for (int i = tid; i < kStages * kBN; i += 64 * kSW) {
-      const int st = i / kBN, row = i % kBN;
-      *reinterpret_cast<uint32_t*>(smem + st * C::STAGE + C::V_OFF + row * C::VROW + CH * 16) = 0x3F80u;
-    }
-  }
-  __syncthreads();
   const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
-  // copy instructions of this wavefront: j = wave, wave+4, ... < NI
-  // (j < KSL: K slots j*64 .. +63; else V slots (j-KSL)*64 .. +63)
+  // Copy instructions of this wavefront: j = wave, wave+4, ... < NI
+  // (j < KSL: K slots j*64 .. +63; else V slots (j-KSL)*64 .. +63). A lane's
+  // source offset inside a tile is fixed; lanes on padding slots copy from
+  // pad_src instead (1.0 at dim d for V rows with the ones column, else
+  // zeros), so every lane of a full tile is active.
   const int n_mine = (C::NI - wave + kSW - 1) / kSW;
   int g_off[C::MAXI], g_row[C::MAXI];
-  bool g_ok[C::MAXI];
+  bool g_pad[C::MAXI];
 #pragma unroll
   for (int i = 0; i < C::MAXI; ++i) {
     const int j = wave + kSW * i;
     const bool isv = j >= KSL;
     const int slot = (isv ? j - KSL : j) * 64 + lane;
     const int row = slot / (isv ? VSL : KSL), c = slot % (isv ? VSL : KSL);
-    g_ok[i] = j < C::NI && c < CH;
+    g_pad[i] = c >= CH;
     g_row[i] = row;
     g_off[i] = row * (int)tok_stride + c * 8;
   }
+  const unsigned char* pad_ones = static_cast<const unsigned char*>(a.pad_src);
+  const unsigned char* pad_zero = pad_ones + 16;
 
   const int tiles_per_frame = (S + kBN - 1) / kBN;
   const int n_tiles = (1 + a.n_prefix) * tiles_per_frame;
-  auto tile_full = [&](int t) { return t < n_tiles && S - (t % tiles_per_frame) * kBN >= kBN; };
-  auto issue_tile = [&](int t) {
-    const int kf = t / tiles_per_frame;
-    const int t0 = (t % tiles_per_frame) * kBN;
-    const int nk = min(kBN, S - t0);
+  // copy stream state (scalar): next tile to copy = (frame kf_c, first key t0_c), into stage st_c
+  int kf_c = 0, t0_c = 0, st_c = 0;
+  auto issue_next = [&]() {
+    const int nk = min(kBN, S - t0_c);
     int64_t off;
     const bf16_t* kb;
     const bf16_t* vb;
-    if (kf == 0) {
+    if (kf_c == 0) {
       off = own_off;
       kb = static_cast<const bf16_t*>(a.k);
       vb = static_cast<const bf16_t*>(a.v);
     } else {
-      off = (((int64_t)b * a.p_slots + a.prefix_slot[kf - 1]) * S) * tok_stride + (int64_t)head * D;
+      off = (((int64_t)b * a.p_slots + a.prefix_slot[kf_c - 1]) * S) * tok_stride + (int64_t)head * D;
       kb = static_cast<const bf16_t*>(a.sp_k);
       vb = static_cast<const bf16_t*>(a.sp_v);
     }
-    off += (int64_t)t0 * tok_stride;
-    const unsigned st = lds_base + (t % kStages) * C::STAGE;
+    off += (int64_t)t0_c * tok_stride;
+    const unsigned st = lds_base + st_c * C::STAGE;
+    const bf16_t* kt = kb + off;
+    const bf16_t* vt = vb + off;
 #pragma unroll
     for (int i = 0; i < C::MAXI; ++i) {
       const int j = wave + kSW * i;
-      if (j < C::NI) {
+      if (j < C::NI) {                                  // uniform per wavefront
         const bool isv = j >= KSL;
         const unsigned dst = st + (isv ? C::V_OFF + (j - KSL) * 1024 : j * 1024);
-        const bf16_t* src = (isv ? vb : kb) + off + g_off[i];
-        if (g_ok[i] && g_row[i] < nk) dma16(src, __builtin_amdgcn_readfirstlane(dst));
+        const void* src = (isv ? vt : kt) + g_off[i];
+        if (g_pad[i]) src = (isv && C::ONES) ? (const void*)pad_ones : (const void*)pad_zero;
+        if (nk == kBN) {
+          dma16(src, dst);
+        } else if (g_row[i] < nk || g_pad[i]) {           // last, partial tile of a frame
+          dma16(src, dst);
+        }
       }
     }
+    t0_c += kBN;
+    if (t0_c >= S) { t0_c = 0; ++kf_c; }
+    st_c = st_c == kStages - 1 ? 0 : st_c + 1;
   };
 
   f32x16 acc[QB][DBLK];
@@ -232,23 +242,27 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { m_run[qb] = kNoMax; l_run[qb] = 0.f; }
 
-  issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
+  issue_next();                                    // tile 0
+  if (kStages == 3 && n_tiles > 1) issue_next();   // tile 1
+  int st_r = 0;                    // stage being read
+  int t0_r = 0;                    // first key of the tile being read (within its frame)
 
   for (int t = 0; t < n_tiles; ++t) {
     // wait for this wavefront's copies of tile t (tile t+1's may stay in
     // flight when it is a full tile, whose copy count is exact), then publish
-    if (tile_full(t + 1) && tile_full(t)) {
+    if (kStages == 3 && S % kBN == 0 && t + 1 < n_tiles) {
       if (n_mine == C::MAXI) wait_vmcnt<C::MAXI>(); else wait_vmcnt<C::MAXI - 1>();
     } else {
       wait_vmcnt<0>();
     }
     lds_barrier();                     // also: every wavefront is done with tile t-1
-    if (t + 2 < n_tiles) issue_tile(t + 2);   // into the stage tile t-1 used
+    if (t + kStages - 1 < n_tiles) issue_next();   // into the stage tile t-1 used
 
-    const unsigned char* ks = smem + (t % kStages) * C::STAGE;
+    const unsigned char* ks = smem + st_r * C::STAGE;
     const unsigned char* vs = ks + C::V_OFF;
-    const int nk = min(kBN, S - (t % tiles_per_frame) * kBN);
+    const int nk = min(kBN, S - t0_r);
+    st_r = st_r == kStages - 1 ? 0 : st_r + 1;
+    t0_r = t0_r + kBN >= S ? 0 : t0_r + kBN;
     const f32x16 zero16 = {};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -433,27 +447,31 @@ __global__ __launch_bounds__(64) void spatial_attn_f32_kernel(SpatialArgs a) {
   }
 }
 
-template <int D, int QB>
-hipError_t launch_mfma_qb(const SpatialArgs& a, hipStream_t s) {
-  constexpr int BM = 32 * QB * kSW;
+template <int D, int QB, int SW, int ST>
+hipError_t launch_mfma_cfg(const SpatialArgs& a, hipStream_t s) {
+  constexpr int BM = 32 * QB * SW;
   const int64_t nwg = (int64_t)((a.tokens + BM - 1) / BM) * a.n * a.heads * a.batch;
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((spatial_attn_mfma_kernel<D, QB>), dim3((unsigned)nwg), dim3(64 * kSW), 0, s, a);
+  hipLaunchKernelGGL((spatial_attn_mfma_kernel<D, QB, SW, ST>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_mfma(const SpatialArgs& a, hipStream_t s) {
-  // Two query blocks of 32 per wavefront halve the LDS operand traffic per
-  // MFMA; used when the grid still gives >= 4 workgroups per CU (and the
-  // registers fit: d <= 72). Both variants run two wavefronts per SIMD.
-  const int64_t wg2 = (int64_t)((a.tokens + 255) / 256) * a.n * a.heads * a.batch;
-  const char* force = getenv("CA2_SPATIAL_QB");
-  const bool qb2 = force ? force[0] == '2' : (D <= 72 && wg2 >= 1024);
+  // Large grids: 4 wavefronts x 64 queries (each LDS operand feeds two MFMAs),
+  // 3-stage ring, 2 workgroups per CU. Small grids (fewer than ~4 such
+  // workgroups per CU): 2 wavefronts x 32 queries with a 2-stage ring, so 4
+  // workgroups fit per CU and every SIMD still runs two wavefronts.
+  const int64_t frames = (int64_t)a.n * a.heads * a.batch;
+  const int64_t wg_big = (int64_t)((a.tokens + 255) / 256) * frames;
+  const char* force = getenv("CA2_SPATIAL_CFG");
+  int cfg = wg_big >= 1024 ? 2 : 1;
+  if (force) cfg = force[0] - '0';
   if constexpr (D <= 72) {
-    if (qb2) return launch_mfma_qb<D, 2>(a, s);
+    if (cfg == 2) return launch_mfma_cfg<D, 2, 4, 3>(a, s);
   }
-  return launch_mfma_qb<D, 1>(a, s);
+  if (cfg == 1) return launch_mfma_cfg<D, 1, 4, 3>(a, s);
+  return launch_mfma_cfg<D, 1, 2, 2>(a, s);
 }
 
 template <int D>
