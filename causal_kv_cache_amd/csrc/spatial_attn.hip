@@ -111,36 +111,61 @@ __device__ __forceinline__ int xcd_work_index(int block, int nblocks) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
 }
 
-// QB query blocks of 32 per wavefront, kSW wavefronts per workgroup (32*QB*kSW
-// queries), kStages-deep LDS ring (prefetch distance kStages-1).
-template <int D, int QB, int kSW, int kStages>
-__global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))) void spatial_attn_mfma_kernel(SpatialArgs a) {
+// Lazy rescale of one query block's running state: only when a lane's new
+// maximum passes its running maximum by more than 2^kLazy. The test is made
+// wave-uniform so that the common case is one scalar branch; inside, lanes
+// that keep their maximum get a factor of exactly 1.
+template <int DBLK>
+__device__ __forceinline__ void lazy_rescale(float mx, float& m_run, float& l_run, f32x16 (&acc)[DBLK]) {
+  const bool need = mx > m_run + kLazy;
+  if (__builtin_amdgcn_ballot_w64(need) == 0) return;
+  const float m_new = need ? mx : m_run;
+  const float corr = fast_exp2(m_run - m_new);
+  m_run = m_new;
+  l_run *= corr;
+#pragma unroll
+  for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] *= corr;
+}
+
+// ----------------------------------------------------------------------------
+// bf16 MFMA kernel, software-pipelined
+// ----------------------------------------------------------------------------
+// Same data movement as above with a 4-stage ring; the work is cut into
+// chunks of 32 keys and reordered so that each wavefront keeps its MFMA and
+// VALU pipes busy at the same time. With S(c) the scores of chunk c:
+//   S(c+1) = K(c+1) Q^T        (MFMA)  ||  P(c) = exp2(S(c) - m)   (VALU)
+//   O     += V(c) P(c)         (MFMA)  ||  max of S(c+1)           (VALU)
+// followed by the (rare) lazy rescale for chunk c+1. Two chunks live in
+// registers at once, which at 32 keys per chunk leaves room for 64 queries
+// per wavefront within 256 registers. The second chunk of tile t+1 is scored
+// during tile t, so tile t+1 must be resident one iteration earlier: at
+// iteration t the wavefront waits for tile t+1's copies and refills the stage
+// of tile t-1 with tile t+3.
+template <int D, int QB, int kSW, bool FULL>
+__global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))) void spatial_attn_pipe_kernel(SpatialArgs a) {
   using C = SCfg<D, kSW>;
-  static_assert(kStages == 2 || kStages == 3, "ring depth");
+  constexpr int kStages = 4;
   constexpr int KSTEPS = C::KSTEPS, DBLK = C::DBLK, KSL = C::KSL, VSL = C::VSL, CH = C::CH;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * C::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps per-wave state scalar
-  const int half = lane >> 5;            // k-half of the MFMA operands
-  const int col = lane & 31;             // query column owned by this lane
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
   const int S = a.tokens;
-  // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
-  // Give every XCD a contiguous run of work items ordered (b, head, frame,
-  // query block), so the query blocks of one frame and the frames sharing the
-  // same prefix frames read their K/V through the same L2.
   const int nq = (S + 32 * QB * kSW - 1) / (32 * QB * kSW);
   const int w = xcd_work_index(blockIdx.x, gridDim.x);
   const int qblk = w % nq;
   const int f = (w / nq) % a.n;
   const int head = (w / (nq * a.n)) % a.heads;
   const int b = w / (nq * a.n * a.heads);
-  const int64_t tok_stride = (int64_t)a.heads * D;           // elements between tokens
+  const int64_t tok_stride = (int64_t)a.heads * D;
   const int64_t own_off = (((int64_t)b * a.n + f) * S) * tok_stride + (int64_t)head * D;
   const int q_base = qblk * (32 * QB * kSW) + wave * (32 * QB);
 
-  // Q^T operands (B of S^T = K Q^T): dims 16s + 8*half .. +7 of each query column
   bf16x8v qop[QB][KSTEPS];
   bool q_ok[QB];
 #pragma unroll
@@ -156,22 +181,24 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
       qop[qb][s] = __builtin_bit_cast(bf16x8v, u);
     }
   }
-
-  // The Q operands must be complete before the copy stream starts: vmcnt also
-  // counts the copies, so a wait for Q inside the loop would drain them too.
-  wait_vmcnt<0>();
-
-  // LDS init: zero everything once (rows past a partial tile stay finite)
-  for (int i = tid; i < kStages * C::STAGE / 16; i += 64 * kSW)
-    reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
   const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  if constexpr (FULL) {
+    // Every key/value slot is rewritten by the copy stream for each tile; only
+    // the 32 bytes past the last K row and the 64 past the last V row (read by
+    // the padded last k-step and by the transposing reads, multiplied by
+    // zeros) are never copied. Zero them so that they cannot hold NaN.
+    if (tid < 6 * kStages) {
+      const int st = tid / 6, k = tid % 6;
+      const int off = st * C::STAGE + (k < 2 ? 64 * C::KROW + 16 * k : C::V_OFF + 64 * C::VROW + 16 * (k - 2));
+      *reinterpret_cast<uint4*>(smem + off) = make_uint4(0, 0, 0, 0);
+    }
+  } else {
+    // partial tiles leave rows uncopied: start from a zeroed ring
+    for (int i = tid; i < kStages * C::STAGE / 16; i += 64 * kSW)
+      reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+  }
 
-  // Copy instructions of this wavefront: j = wave, wave+4, ... < NI
-  // (j < KSL: K slots j*64 .. +63; else V slots (j-KSL)*64 .. +63). A lane's
-  // source offset inside a tile is fixed; lanes on padding slots copy from
-  // pad_src instead (1.0 at dim d for V rows with the ones column, else
-  // zeros), so every lane of a full tile is active.
   const int n_mine = (C::NI - wave + kSW - 1) / kSW;
   int g_off[C::MAXI], g_row[C::MAXI];
   bool g_pad[C::MAXI];
@@ -187,10 +214,8 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
   }
   const unsigned char* pad_ones = static_cast<const unsigned char*>(a.pad_src);
   const unsigned char* pad_zero = pad_ones + 16;
-
   const int tiles_per_frame = (S + kBN - 1) / kBN;
   const int n_tiles = (1 + a.n_prefix) * tiles_per_frame;
-  // copy stream state (scalar): next tile to copy = (frame kf_c, first key t0_c), into stage st_c
   int kf_c = 0, t0_c = 0, st_c = 0;
   auto issue_next = [&]() {
     const int nk = min(kBN, S - t0_c);
@@ -213,21 +238,28 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
     for (int i = 0; i < C::MAXI; ++i) {
       const int j = wave + kSW * i;
-      if (j < C::NI) {                                  // uniform per wavefront
+      if (j < C::NI) {
         const bool isv = j >= KSL;
         const unsigned dst = st + (isv ? C::V_OFF + (j - KSL) * 1024 : j * 1024);
         const void* src = (isv ? vt : kt) + g_off[i];
         if (g_pad[i]) src = (isv && C::ONES) ? (const void*)pad_ones : (const void*)pad_zero;
-        if (nk == kBN) {
-          dma16(src, dst);
-        } else if (g_row[i] < nk || g_pad[i]) {           // last, partial tile of a frame
-          dma16(src, dst);
-        }
+        if (FULL || nk == kBN || g_row[i] < nk || g_pad[i]) dma16(src, dst);
       }
     }
     t0_c += kBN;
     if (t0_c >= S) { t0_c = 0; ++kf_c; }
     st_c = st_c == kStages - 1 ? 0 : st_c + 1;
+  };
+  // wait until this wavefront's copies of the oldest outstanding tile are done
+  // while `ahead` younger tiles stay in flight (exact counts need full tiles)
+  auto wait_tiles = [&](int ahead) {
+    if (FULL && ahead == 2) {
+      if (n_mine == C::MAXI) wait_vmcnt<2 * C::MAXI>(); else wait_vmcnt<2 * (C::MAXI - 1)>();
+    } else if (FULL && ahead == 1) {
+      if (n_mine == C::MAXI) wait_vmcnt<C::MAXI>(); else wait_vmcnt<C::MAXI - 1>();
+    } else {
+      wait_vmcnt<0>();
+    }
   };
 
   f32x16 acc[QB][DBLK];
@@ -237,119 +269,132 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
     for (int i = 0; i < DBLK; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[qb][i][r] = 0.f;
-  float m_run[QB];
-  float l_run[QB];            // explicit row sums (only without the ones column)
+  float m_run[QB], l_run[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { m_run[qb] = kNoMax; l_run[qb] = 0.f; }
 
-  issue_next();                                    // tile 0
-  if (kStages == 3 && n_tiles > 1) issue_next();   // tile 1
-  int st_r = 0;                    // stage being read
-  int t0_r = 0;                    // first key of the tile being read (within its frame)
-
-  for (int t = 0; t < n_tiles; ++t) {
-    // wait for this wavefront's copies of tile t (tile t+1's may stay in
-    // flight when it is a full tile, whose copy count is exact), then publish
-    if (kStages == 3 && S % kBN == 0 && t + 1 < n_tiles) {
-      if (n_mine == C::MAXI) wait_vmcnt<C::MAXI>(); else wait_vmcnt<C::MAXI - 1>();
-    } else {
-      wait_vmcnt<0>();
+  const f32x16 zero16 = {};
+  // S^T = K Q^T for keys kb*32 .. +31 of a tile: sc[qb] register r holds key
+  // kb*32 + 8(r/4) + 4*half + r%4 of query 32*qb + col
+  auto qk = [&](const unsigned char* ks, int kb, f32x16 (&sc)[QB]) {
+    const unsigned char* krow = ks + (kb * 32 + col) * C::KROW;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const bf16x8v kop = *reinterpret_cast<const bf16x8v*>(krow + (16 * s + 8 * half) * 2);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[qb][s], s == 0 ? zero16 : sc[qb], 0, 0, 0);
     }
-    lds_barrier();                     // also: every wavefront is done with tile t-1
-    if (t + kStages - 1 < n_tiles) issue_next();   // into the stage tile t-1 used
-
-    const unsigned char* ks = smem + st_r * C::STAGE;
-    const unsigned char* vs = ks + C::V_OFF;
-    const int nk = min(kBN, S - t0_r);
-    st_r = st_r == kStages - 1 ? 0 : st_r + 1;
-    t0_r = t0_r + kBN >= S ? 0 : t0_r + kBN;
-    const f32x16 zero16 = {};
+  };
+  auto mask_tail = [&](f32x16 (&sc)[QB], int kb, int nk) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // -- S^T = K Q^T for keys kb*32 .. +31 --
-      f32x16 sc[QB];
-      const unsigned char* krow = ks + (kb * 32 + col) * C::KROW;
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8v kop = *reinterpret_cast<const bf16x8v*>(krow + (16 * s + 8 * half) * 2);
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= nk) sc[qb][r] = -INFINITY;
+  };
+  // chunk max (scaled, base 2) and lazy rescale of the running state
+  auto max_rescale = [&](const f32x16 (&sc)[QB]) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[qb][s], s == 0 ? zero16 : sc[qb], 0, 0, 0);
-      }
-      // register r of sc[.] holds key kb*32 + 8*(r/4) + 4*half + r%4
-      if (nk < kBN) {
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = __builtin_fmaxf(sc[qb][0], sc[qb][1]);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+      for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[qb][r]), sc[qb][r + 1]);
+      mx = max_halves(mx) * a.scale_log2e;
+      lazy_rescale(mx, m_run[qb], l_run[qb], acc[qb]);
+    }
+  };
+  // P of one chunk as the B operands of two 16-key k-steps
+  auto expc = [&](const f32x16 (&sc)[QB], bf16x8v (&pf)[QB][2]) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key >= nk) sc[qb][r] = -INFINITY;
-          }
-      }
-      bf16x8v pf[QB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = __builtin_fmaxf(sc[qb][0], sc[qb][1]);
-#pragma unroll
-        for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[qb][r]), sc[qb][r + 1]);
-        mx = max_halves(mx) * a.scale_log2e;
-        // lazy rescale: only when the max passes the running max by > 2^8
-        if (mx > m_run[qb] + kLazy) {
-          const float corr = fast_exp2(m_run[qb] - mx);
-          m_run[qb] = mx;
-          l_run[qb] *= corr;
-#pragma unroll
-          for (int i = 0; i < DBLK; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[qb][i][r] *= corr;
-        }
-        const float mneg = -m_run[qb];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          uint32_t wv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = fast_exp2(fmaf(sc[qb][8 * h2 + 2 * e], a.scale_log2e, mneg));
-            const float p1 = fast_exp2(fmaf(sc[qb][8 * h2 + 2 * e + 1], a.scale_log2e, mneg));
-            if constexpr (!C::ONES) l_run[qb] += p0 + p1;
-            wv[e] = pack_bf16x2(p0, p1);
-          }
-          pf[qb][h2] = __builtin_bit_cast(bf16x8v, make_uint4(wv[0], wv[1], wv[2], wv[3]));
-        }
-      }
-      // -- O^T += V^T P^T over these 32 keys, k-steps of 16 (mm = 2kb + h2).
-      //    Element e of the operands is key 16mm + 4*half + e (+4 for e >= 4).
-      //    Transposing read: lane 16g + j addresses key row 16mm + 4*(g/2) +
-      //    j/4 (+8 for the second read) at dims 32i + 16*(g%2) + 4*(j%4); it
-      //    receives dim 32i + (lane%32) of keys 16mm + 4*(g/2) + 0..3.
-      const int g16 = lane >> 4, j16 = lane & 15;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mneg = -m_run[qb];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const int mm = 2 * kb + h2;
+        uint32_t wv[4];
 #pragma unroll
-        for (int i = 0; i < DBLK; ++i) {
-          const unsigned char* p0 = vs + (16 * mm + 4 * (g16 >> 1) + (j16 >> 2)) * C::VROW +
-                                    (32 * i + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
-          const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
-          const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 8 * C::VROW));
-          const bf16x8v vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            acc[qb][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf[qb][h2], acc[qb][i], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(fmaf(sc[qb][8 * h2 + 2 * e], a.scale_log2e, mneg));
+          const float p1 = fast_exp2(fmaf(sc[qb][8 * h2 + 2 * e + 1], a.scale_log2e, mneg));
+          if constexpr (!C::ONES) l_run[qb] += p0 + p1;
+          wv[e] = pack_bf16x2(p0, p1);
         }
+        pf[qb][h2] = __builtin_bit_cast(bf16x8v, make_uint4(wv[0], wv[1], wv[2], wv[3]));
       }
     }
+  };
+  const int g16 = lane >> 4, j16 = lane & 15;
+  auto pv = [&](const unsigned char* vs, int kb, const bf16x8v (&pf)[QB][2]) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int mm = 2 * kb + h2;
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) {
+        const unsigned char* p0 = vs + (16 * mm + 4 * (g16 >> 1) + (j16 >> 2)) * C::VROW +
+                                  (32 * i + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
+        const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+        const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 8 * C::VROW));
+        const bf16x8v vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          acc[qb][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf[qb][h2], acc[qb][i], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- prologue: tile 0 copied while Q is loaded, tiles 1..2 in flight, first chunk scored ----
+  issue_next();
+  wait_vmcnt<0>();   // Q and this wavefront's copies of tile 0 (the loop's waits count copies only)
+  if (n_tiles > 1) issue_next();
+  if (n_tiles > 2) issue_next();
+  lds_barrier();
+  f32x16 s0[QB], s1[QB];
+  bf16x8v pf[QB][2];
+  int nk_t = min(kBN, S);             // keys in tile t
+  qk(smem, 0, s0);
+  if (!FULL && nk_t < 32) mask_tail(s0, 0, nk_t);
+  max_rescale(s0);
+
+  int st_r = 0;                       // stage of tile t
+  int t0_n = kBN >= S ? 0 : kBN;      // first key of tile t+1 within its frame
+  for (int t = 0; t + 1 < n_tiles; ++t) {
+    const unsigned char* ks = smem + st_r * C::STAGE;
+    const unsigned char* vs = ks + C::V_OFF;
+    // chunk 2t+1 (same tile) is scored while chunk 2t is exponentiated
+    qk(ks, 1, s1);
+    expc(s0, pf);
+    pv(vs, 0, pf);
+    if (!FULL && nk_t < kBN) mask_tail(s1, 1, nk_t);
+    max_rescale(s1);
+    st_r = st_r == kStages - 1 ? 0 : st_r + 1;
+    wait_tiles(t + 2 < n_tiles ? 1 : 0);   // tile t+1 (t+2 may stay in flight)
+    lds_barrier();                          // every wavefront is done with tile t-1
+    if (t + 3 < n_tiles) issue_next();      // tile t+3 into tile t-1's stage
+    // chunk 2t+2 (next tile) is scored while chunk 2t+1 is exponentiated
+    qk(smem + st_r * C::STAGE, 0, s0);
+    expc(s1, pf);
+    pv(vs, 1, pf);
+    nk_t = min(kBN, S - t0_n);
+    if (!FULL && nk_t < 32) mask_tail(s0, 0, nk_t);
+    max_rescale(s0);
+    t0_n = t0_n + kBN >= S ? 0 : t0_n + kBN;
+  }
+  {  // last tile
+    const unsigned char* ks = smem + st_r * C::STAGE;
+    const unsigned char* vs = ks + C::V_OFF;
+    qk(ks, 1, s1);
+    expc(s0, pf);
+    pv(vs, 0, pf);
+    if (!FULL && nk_t < kBN) mask_tail(s1, 1, nk_t);
+    max_rescale(s1);
+    expc(s1, pf);
+    pv(vs, 1, pf);
   }
 
-  // -- normalise and write: register r of acc[.][i] is dim 32i + 8(r/4) + 4*half + r%4 --
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     float l_tot;
     if constexpr (C::ONES) {
-      // row sum = O^T row D (the ones column): register 4*((D%32)/8) + D%4 of
-      // block D/32 in the lanes of half 0; the same register of half 1 holds
-      // row D+4, whose V column is zero padding, so adding the halves gives
-      // the sum in every lane
       constexpr int RD = D % 32;
       constexpr int REG = 4 * (RD / 8) + (RD % 4);
       static_assert(RD % 8 == 0 && D + 4 < C::DP, "row D+4 must be a zero padding row");
@@ -447,31 +492,32 @@ __global__ __launch_bounds__(64) void spatial_attn_f32_kernel(SpatialArgs a) {
   }
 }
 
-template <int D, int QB, int SW, int ST>
-hipError_t launch_mfma_cfg(const SpatialArgs& a, hipStream_t s) {
+template <int D, int QB, int SW>
+hipError_t launch_pipe_cfg(const SpatialArgs& a, hipStream_t s) {
   constexpr int BM = 32 * QB * SW;
   const int64_t nwg = (int64_t)((a.tokens + BM - 1) / BM) * a.n * a.heads * a.batch;
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((spatial_attn_mfma_kernel<D, QB, SW, ST>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
+  if (a.tokens % kBN == 0)
+    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, true>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
+  else
+    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, false>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_mfma(const SpatialArgs& a, hipStream_t s) {
-  // Large grids: 4 wavefronts x 64 queries (each LDS operand feeds two MFMAs),
-  // 3-stage ring, 2 workgroups per CU. Small grids (fewer than ~4 such
-  // workgroups per CU): 2 wavefronts x 32 queries with a 2-stage ring, so 4
-  // workgroups fit per CU and every SIMD still runs two wavefronts.
+  // 64 queries per wavefront (each K/V operand read from LDS feeds two MFMAs)
+  // once the grid has at least ~4 such workgroups per CU; 32 per wavefront
+  // below that, which doubles the number of wavefronts in flight.
+  // CA2_SPATIAL_QB=1|2 forces either.
   const int64_t frames = (int64_t)a.n * a.heads * a.batch;
   const int64_t wg_big = (int64_t)((a.tokens + 255) / 256) * frames;
-  const char* force = getenv("CA2_SPATIAL_CFG");
-  int cfg = wg_big >= 1024 ? 2 : 1;
-  if (force) cfg = force[0] - '0';
+  int qb = wg_big >= 1024 ? 2 : 1;
+  if (const char* force = getenv("CA2_SPATIAL_QB")) qb = force[0] - '0';
   if constexpr (D <= 72) {
-    if (cfg == 2) return launch_mfma_cfg<D, 2, 4, 3>(a, s);
+    if (qb == 2) return launch_pipe_cfg<D, 2, 4>(a, s);
   }
-  if (cfg == 1) return launch_mfma_cfg<D, 1, 4, 3>(a, s);
-  return launch_mfma_cfg<D, 1, 2, 2>(a, s);
+  return launch_pipe_cfg<D, 1, 4>(a, s);
 }
 
 template <int D>

@@ -384,16 +384,17 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
     for (int e = 0; e < DPL; ++e) acc[qq][e] = 0.f;
   }
 
-  Slice<D> kc, vc, kn, vn;
-  if (row_ok && kb < ke) {
-    load_slice<D>(kc, key_row(kb, rkb, knb), g);
-    load_slice<D>(vc, key_row(kb, rvb, vnb), g);
-  }
-  for (int j = kb; j < ke; ++j) {
-    if (row_ok && j + 1 < ke) {
-      load_slice<D>(kn, key_row(j + 1, rkb, knb), g);
-      load_slice<D>(vn, key_row(j + 1, rvb, vnb), g);
+  // K/V slices of keys j .. j+3 in a 4-slot register ring: key j+3 is loaded
+  // while key j is processed, so three keys per lane are always in flight.
+  constexpr int kPF = 4;
+  Slice<D> kr[kPF], vr[kPF];
+#pragma unroll
+  for (int u = 0; u < kPF - 1; ++u)
+    if (row_ok && kb + u < ke) {
+      load_slice<D>(kr[u], key_row(kb + u, rkb, knb), g);
+      load_slice<D>(vr[u], key_row(kb + u, rvb, vnb), g);
     }
+  auto process = [&](int j, const Slice<D>& kc, const Slice<D>& vc) {
     // scores of the lane's queries against key j
     float x[kQPL];
     bool raise = false;
@@ -432,8 +433,19 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[qq][e] = fmaf(p, v[e], acc[qq][e]);
     }
-    kc = kn;
-    vc = vn;
+  };
+  for (int j = kb; j < ke; j += kPF) {
+#pragma unroll
+    for (int u = 0; u < kPF; ++u) {
+      if (j + u < ke) {                                  // uniform per wavefront
+        const int jn = j + u + kPF - 1;
+        if (row_ok && jn < ke) {
+          load_slice<D>(kr[(u + kPF - 1) % kPF], key_row(jn, rkb, knb), g);
+          load_slice<D>(vr[(u + kPF - 1) % kPF], key_row(jn, rvb, vnb), g);
+        }
+        process(j + u, kr[u], vr[u]);
+      }
+    }
   }
 
   // merge the wavefronts of a split key range
