@@ -37,6 +37,7 @@ METRIC = "attention tokens/sec per denoise step; temporal HBM GB/s, spatial MFMA
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
 T_DENOISE = 50
+N_CACHES = 8      # per-layer caches rotated through at the 256-token shape
 
 AR_STEP = dict(name="ar_step_s256", B=1, H=16, d=72, S=256, l=8, p_max=25, p_spatial=3, tpe_len=33)
 LARGE = dict(name="large_b8_s1024", B=8, H=16, d=72, S=1024, l=8, p_max=25, p_spatial=3, tpe_len=33)
@@ -83,44 +84,56 @@ def _randn(shape, gen, dtype):
 
 
 class Workload:
-    """Device buffers and a cache filled to P_max for one shape."""
+    """Device buffers and `n_caches` caches filled to P_max for one shape.
 
-    def __init__(self, sh, n_sets, seed):
+    Several caches stand for the per-layer caches of a model: consecutive
+    denoising calls use consecutive caches, and each cache-writing pass writes
+    the next one, so the rotated working set (caches plus Q/K/V sets) exceeds
+    the 256 MB Infinity Cache and the temporal reads are served by HBM."""
+
+    def __init__(self, sh, n_sets, seed, n_caches=1):
         import torch
         from causal_kv_cache_amd import ca2
         self.sh = sh
-        self.cache = ca2.Cache(sh["B"], sh["H"], sh["d"], sh["S"], sh["l"], sh["p_max"],
-                               sh["p_spatial"], sh["tpe_len"], "bf16")
         gen = torch.Generator(device="cuda")
         gen.manual_seed(seed)
         bf = torch.bfloat16
         B, l, S, H, d = sh["B"], sh["l"], sh["S"], sh["H"], sh["d"]
         chunk = (B, l, S, H, d)
-        # fill the queue: conditioning frame, then whole chunks, to P_max frames
-        frames = 0
-        while frames < sh["p_max"]:
-            w = 1 if frames == 0 else l
-            t = [_randn((B, w, S, H, d), gen, bf) for _ in range(4)]
-            self.cache.ca2_cache_write(*t)
-            frames += w
+        self.caches = []
+        for _ in range(n_caches):
+            c = ca2.Cache(B, H, d, S, l, sh["p_max"], sh["p_spatial"], sh["tpe_len"], "bf16")
+            # fill the queue: conditioning frame, then whole chunks, to P_max frames
+            frames = 0
+            while frames < sh["p_max"]:
+                w = 1 if frames == 0 else l
+                t = [_randn((B, w, S, H, d), gen, bf) for _ in range(4)]
+                c.ca2_cache_write(*t)
+                frames += w
+            self.caches.append(c)
+        self.cache = self.caches[0]
         self.sets = [tuple(_randn(chunk, gen, bf) for _ in range(3)) for _ in range(n_sets)]
         self.clean = tuple(_randn(chunk, gen, bf) for _ in range(5))   # qc, kt, vt, ks, vs
         self.out_t = torch.empty(chunk, dtype=bf, device="cuda")
         self.out_s = torch.empty(chunk, dtype=bf, device="cuda")
+        self.passes = 0
         torch.cuda.synchronize()
 
     def denoise(self, i):
         q, k, v = self.sets[i % len(self.sets)]
-        self.cache.ca2_spatial_attn(q, k, v, self.out_s)
-        self.cache.ca2_temporal_attn(q, k, v, self.out_t)
+        c = self.caches[i % len(self.caches)]
+        c.ca2_spatial_attn(q, k, v, self.out_s)
+        c.ca2_temporal_attn(q, k, v, self.out_t)
 
     def write_pass(self):
         from causal_kv_cache_amd import ca2
         qc, kt, vt, ks, vs = self.clean
-        self.cache.ca2_tpe_index(self.sh["l"])
-        self.cache.ca2_temporal_attn(qc, kt, vt, self.out_t)
-        self.cache.ca2_spatial_attn(qc, ks, vs, self.out_s, mode=ca2.CA2_SPATIAL_SELF)
-        self.cache.ca2_cache_write(kt, vt, ks, vs)
+        c = self.caches[self.passes % len(self.caches)]
+        self.passes += 1
+        c.ca2_tpe_index(self.sh["l"])
+        c.ca2_temporal_attn(qc, kt, vt, self.out_t)
+        c.ca2_spatial_attn(qc, ks, vs, self.out_s, mode=ca2.CA2_SPATIAL_SELF)
+        c.ca2_cache_write(kt, vt, ks, vs)
 
     def ar_step(self):
         for t in range(T_DENOISE):
@@ -148,23 +161,23 @@ def kernel_table(w: Workload, reps: int):
     from causal_kv_cache_amd import ca2
     sh = w.sh
     n, pk, ps = sh["l"], sh["p_max"], sh["p_spatial"]
-    c = w.cache
-    sets = w.sets
+    sets, caches = w.sets, w.caches
     idx = [0]
 
     def nxt():
         idx[0] += 1
-        return sets[idx[0] % len(sets)]
+        return caches[idx[0] % len(caches)], sets[idx[0] % len(sets)]
 
     def k_spatial():
-        q, k, v = nxt()
+        c, (q, k, v) = nxt()
         c.ca2_spatial_attn(q, k, v, w.out_s)
 
     def k_temporal():
-        q, k, v = nxt()
+        c, (q, k, v) = nxt()
         c.ca2_temporal_attn(q, k, v, w.out_t)
 
     def k_spatial_self():
+        c, _ = nxt()
         qc, kt, vt, ks, vs = w.clean
         c.ca2_spatial_attn(qc, ks, vs, w.out_s, mode=ca2.CA2_SPATIAL_SELF)
 
@@ -318,7 +331,7 @@ def main():
         print(json.dumps(kernel_mode(args.kernel, args.workload, args.reps)), flush=True)
         return
 
-    w = Workload(AR_STEP, T_DENOISE, seed=1234)
+    w = Workload(AR_STEP, T_DENOISE, seed=1234, n_caches=N_CACHES)
     for _ in range(args.warmup):
         w.ar_step()
     torch.cuda.synchronize()

@@ -30,7 +30,6 @@ struct ca2_cache {
   void* ring_v;
   void* sp_k;
   void* sp_v;
-  void* pad_src;         // 32 B constant source for padding slots of staged V rows
 };
 
 namespace {
@@ -152,9 +151,9 @@ ca2_status ca2_cache_create(const ca2_config* cfg, ca2_cache** out) {
   // CA2_NAN_CANARY=1, so a kernel reading a slot it should not shows up as NaN.
   const char* canary = getenv("CA2_NAN_CANARY");
   const int fill = (canary && canary[0] == '1') ? 0xFF : 0x00;
-  void** bufs[5] = {&c->ring_k, &c->ring_v, &c->sp_k, &c->sp_v, &c->pad_src};
-  const size_t sizes[5] = {ring_bytes, ring_bytes, sp_bytes, sp_bytes, 256};
-  for (int i = 0; i < 5; ++i) {
+  void** bufs[4] = {&c->ring_k, &c->ring_v, &c->sp_k, &c->sp_v};
+  const size_t sizes[4] = {ring_bytes, ring_bytes, sp_bytes, sp_bytes};
+  for (int i = 0; i < 4; ++i) {
     *bufs[i] = nullptr;
     if (!sizes[i]) continue;
     hipError_t e = hipMalloc(bufs[i], sizes[i]);
@@ -164,18 +163,10 @@ ca2_status ca2_cache_create(const ca2_config* cfg, ca2_cache** out) {
       return e == hipErrorOutOfMemory ? fail(CA2_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) failed", sizes[i])
                                       : hip_fail(e, "hipMalloc");
     }
-    e = hipMemset(*bufs[i], i < 4 ? fill : 0, sizes[i]);
+    e = hipMemset(*bufs[i], fill, sizes[i]);
     if (e != hipSuccess) {
       ca2_cache_destroy(c);
       return hip_fail(e, "hipMemset");
-    }
-  }
-  {
-    const uint16_t one_bf16 = 0x3F80;   // 1.0 in bfloat16, first element of the padding source
-    hipError_t e = hipMemcpy(c->pad_src, &one_bf16, sizeof(one_bf16), hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-      ca2_cache_destroy(c);
-      return hip_fail(e, "hipMemcpy");
     }
   }
   *out = c;
@@ -188,7 +179,6 @@ void ca2_cache_destroy(ca2_cache* c) {
   if (c->ring_v) (void)hipFree(c->ring_v);
   if (c->sp_k) (void)hipFree(c->sp_k);
   if (c->sp_v) (void)hipFree(c->sp_v);
-  if (c->pad_src) (void)hipFree(c->pad_src);
   delete c;
 }
 
@@ -288,7 +278,6 @@ ca2_status ca2_spatial_attn(const ca2_cache* c, const void* q, const void* k, co
     for (int32_t j = 0; j < Ps; ++j) a.prefix_slot[j] = (int32_t)(spatial_frame(c->frames_written, Ps, j) % Ps);
   }
   a.scale_log2e = scale * 1.4426950408889634f;
-  a.pad_src = c->pad_src;
   hipError_t e = ca2::launch_spatial(c->cfg.dtype, c->cfg.head_dim, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "spatial_attn launch");
   return ok();

@@ -37,7 +37,6 @@ struct SpatialArgs {
   int32_t n_prefix;        // prefix frames used (0 in self mode)
   int32_t prefix_slot[16]; // logical -> physical slot
   float scale_log2e;
-  const void* pad_src;     // 32 bytes: bf16 {1,0,0,0,0,0,0,0} then 16 zero bytes
 };
 
 // Bitwise frame copies for the cache write. Job j copies `frame_elems`

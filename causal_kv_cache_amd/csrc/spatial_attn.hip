@@ -93,6 +93,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt vmcnt(ahead * per) for a wave-uniform ahead in [0, kMax]; the
+// count must be an immediate, so each value gets its own instruction.
+template <int per, int k = 0, int kMax = 8>
+__device__ __forceinline__ void wait_vmcnt_tiles(int ahead) {
+  if constexpr (k > kMax || k * per > 63) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead == k) wait_vmcnt<k * per>();
+    else wait_vmcnt_tiles<per, k + 1, kMax>(ahead);
+  }
+}
+
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -132,22 +144,51 @@ __device__ __forceinline__ void lazy_rescale(float mx, float& m_run, float& l_ru
 // ----------------------------------------------------------------------------
 // bf16 MFMA kernel, software-pipelined
 // ----------------------------------------------------------------------------
-// Same data movement as above with a 4-stage ring; the work is cut into
-// chunks of 32 keys and reordered so that each wavefront keeps its MFMA and
-// VALU pipes busy at the same time. With S(c) the scores of chunk c:
+// Data movement: key tiles of 64 keys stream through a kStages-deep LDS ring,
+// row-major (K rows KROW bytes, V rows VROW bytes, both padded for
+// conflict-free reads). A tile is copied HBM -> LDS by global_load_lds_dwordx4
+// (asynchronous, 16 bytes per lane, no register staging): copy instruction j
+// of a tile covers 16-byte slots 64j .. 64j+63 of the tile's rows, so each
+// lane's global offset from the tile base is a constant, and the tile base is
+// a wavefront-uniform 64-bit value -- issuing a tile takes scalar
+// instructions only. Padding slots (zeros, and for d % 32 != 0 a 1.0 at dim
+// d that turns row d of the PV accumulator into the softmax row sum) are
+// written once at the start and never copied over (their lanes are masked).
+// A wavefront waits only for its own copies of the tile it needs (s_waitcnt
+// vmcnt), then one barrier per tile publishes it.
+//
+// Compute: each wavefront cuts a tile into two chunks of 32 keys and, with
+// S(c) the scores of chunk c, overlaps
 //   S(c+1) = K(c+1) Q^T        (MFMA)  ||  P(c) = exp2(S(c) - m)   (VALU)
 //   O     += V(c) P(c)         (MFMA)  ||  max of S(c+1)           (VALU)
-// followed by the (rare) lazy rescale for chunk c+1. Two chunks live in
-// registers at once, which at 32 keys per chunk leaves room for 64 queries
-// per wavefront within 256 registers. The second chunk of tile t+1 is scored
-// during tile t, so tile t+1 must be resident one iteration earlier: at
-// iteration t the wavefront waits for tile t+1's copies and refills the stage
-// of tile t-1 with tile t+3.
-template <int D, int QB, int kSW, bool FULL>
+// then the (rare) lazy rescale for chunk c+1. The second chunk of tile t+1 is
+// scored during tile t, so tile t+1 must be resident one iteration early: at
+// iteration t a wavefront waits for its copies of tile t+1 and, after the
+// barrier, refills the stage of tile t-1 with tile t+kStages-1.
+
+// A wavefront-uniform 64-bit value as such (readfirstlane returns int: widen
+// through unsigned, never sign-extend).
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v >> 32));
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
+// 16-byte global -> LDS copy for every active lane: lane i reads
+// sbase + voff (+ 0..15) and writes lds_addr + 16*i (lds_addr in M0);
+// sbase and lds_addr are wavefront-uniform.
+__device__ __forceinline__ void dma16s(unsigned voff, uint64_t sbase, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(uniform64(sbase)), "s"((unsigned)__builtin_amdgcn_readfirstlane((int)lds_addr))
+               : "memory", "m0");
+}
+
+template <int D, int QB, int kSW, bool FULL, int kStages>
 __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))) void spatial_attn_pipe_kernel(SpatialArgs a) {
   using C = SCfg<D, kSW>;
-  constexpr int kStages = 4;
+  static_assert(kStages >= 3, "the pipeline reads tile t+1 while tile t+2 is copied");
   constexpr int KSTEPS = C::KSTEPS, DBLK = C::DBLK, KSL = C::KSL, VSL = C::VSL, CH = C::CH;
+  constexpr int MAXI = C::MAXI;                    // copies per wavefront per tile (upper bound)
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * C::STAGE];
 
   const int tid = threadIdx.x;
@@ -182,84 +223,89 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
   }
   const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
-  if constexpr (FULL) {
-    // Every key/value slot is rewritten by the copy stream for each tile; only
-    // the 32 bytes past the last K row and the 64 past the last V row (read by
-    // the padded last k-step and by the transposing reads, multiplied by
-    // zeros) are never copied. Zero them so that they cannot hold NaN.
-    if (tid < 6 * kStages) {
-      const int st = tid / 6, k = tid % 6;
-      const int off = st * C::STAGE + (k < 2 ? 64 * C::KROW + 16 * k : C::V_OFF + 64 * C::VROW + 16 * (k - 2));
-      *reinterpret_cast<uint4*>(smem + off) = make_uint4(0, 0, 0, 0);
+  // Padding slots and the bytes past the last K / V row are never copied:
+  // write them once. Partial tiles also leave key rows uncopied, so without
+  // full tiles the whole ring starts zeroed.
+  for (int i = tid; i < kStages * C::STAGE / 16; i += 64 * kSW) {
+    const int off = (i * 16) % C::STAGE;
+    bool pad, ones = false;
+    if (off < C::V_OFF) {
+      const int r = off / C::KROW, c = (off % C::KROW) / 16;
+      pad = r >= kBN || c >= CH;
+    } else {
+      const int o = off - C::V_OFF, r = o / C::VROW, c = (o % C::VROW) / 16;
+      pad = r >= kBN || c >= CH;
+      ones = C::ONES && r < kBN && c == CH;
     }
-  } else {
-    // partial tiles leave rows uncopied: start from a zeroed ring
-    for (int i = tid; i < kStages * C::STAGE / 16; i += 64 * kSW)
-      reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
-    __syncthreads();
+    if (!FULL || pad) reinterpret_cast<uint4*>(smem)[i] = make_uint4(ones ? 0x3F80u : 0u, 0, 0, 0);
   }
-
+  if constexpr (!FULL) __syncthreads();   // zeros land before any copy
+  // copy stream: per-lane byte offsets of each of this wavefront's copy
+  // instructions from the tile base (tile-independent), padding lanes masked
   const int n_mine = (C::NI - wave + kSW - 1) / kSW;
-  int g_off[C::MAXI], g_row[C::MAXI];
-  bool g_pad[C::MAXI];
+  const unsigned row_bytes = (unsigned)(tok_stride * 2);
+  unsigned g_off[MAXI];
+  int g_row[MAXI];
+  bool g_pad[MAXI];
 #pragma unroll
-  for (int i = 0; i < C::MAXI; ++i) {
+  for (int i = 0; i < MAXI; ++i) {
     const int j = wave + kSW * i;
     const bool isv = j >= KSL;
     const int slot = (isv ? j - KSL : j) * 64 + lane;
     const int row = slot / (isv ? VSL : KSL), c = slot % (isv ? VSL : KSL);
     g_pad[i] = c >= CH;
     g_row[i] = row;
-    g_off[i] = row * (int)tok_stride + c * 8;
+    g_off[i] = (unsigned)row * row_bytes + 16u * c;
   }
-  const unsigned char* pad_ones = static_cast<const unsigned char*>(a.pad_src);
-  const unsigned char* pad_zero = pad_ones + 16;
+  // tile base pointers (bytes, this head, key 0 of the tile); the empty asm
+  // keeps the argument pointers from being re-read per tile
+  const unsigned char* sp_k = static_cast<const unsigned char*>(a.sp_k);
+  const unsigned char* sp_v = static_cast<const unsigned char*>(a.sp_v);
+  const unsigned char* fk = static_cast<const unsigned char*>(a.k) + own_off * 2;
+  const unsigned char* fv = static_cast<const unsigned char*>(a.v) + own_off * 2;
+  // prefix slots (< 16 each) packed 4 bits apiece into one scalar
+  uint64_t pslots = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pslots |= (uint64_t)(a.prefix_slot[i] & 15) << (4 * i);
+  asm volatile("" : "+s"(sp_k), "+s"(sp_v), "+s"(fk), "+s"(fv), "+s"(pslots));
+  const int64_t pbase = ((int64_t)b * a.p_slots * S) * tok_stride * 2 + (int64_t)head * D * 2;
+  const int64_t tile_bytes = (int64_t)kBN * tok_stride * 2;
   const int tiles_per_frame = (S + kBN - 1) / kBN;
   const int n_tiles = (1 + a.n_prefix) * tiles_per_frame;
   int kf_c = 0, t0_c = 0, st_c = 0;
   auto issue_next = [&]() {
-    const int nk = min(kBN, S - t0_c);
-    int64_t off;
-    const bf16_t* kb;
-    const bf16_t* vb;
-    if (kf_c == 0) {
-      off = own_off;
-      kb = static_cast<const bf16_t*>(a.k);
-      vb = static_cast<const bf16_t*>(a.v);
-    } else {
-      off = (((int64_t)b * a.p_slots + a.prefix_slot[kf_c - 1]) * S) * tok_stride + (int64_t)head * D;
-      kb = static_cast<const bf16_t*>(a.sp_k);
-      vb = static_cast<const bf16_t*>(a.sp_v);
-    }
-    off += (int64_t)t0_c * tok_stride;
     const unsigned st = lds_base + st_c * C::STAGE;
-    const bf16_t* kt = kb + off;
-    const bf16_t* vt = vb + off;
+    const uint64_t bk = uniform64(reinterpret_cast<uint64_t>(fk));
+    const uint64_t bv = uniform64(reinterpret_cast<uint64_t>(fv));
+    const int nk = S - t0_c;
 #pragma unroll
-    for (int i = 0; i < C::MAXI; ++i) {
+    for (int i = 0; i < MAXI; ++i) {
       const int j = wave + kSW * i;
-      if (j < C::NI) {
+      if (j < C::NI) {                                  // uniform per wavefront
         const bool isv = j >= KSL;
         const unsigned dst = st + (isv ? C::V_OFF + (j - KSL) * 1024 : j * 1024);
-        const void* src = (isv ? vt : kt) + g_off[i];
-        if (g_pad[i]) src = (isv && C::ONES) ? (const void*)pad_ones : (const void*)pad_zero;
-        if (FULL || nk == kBN || g_row[i] < nk || g_pad[i]) dma16(src, dst);
+        if (!g_pad[i] && (FULL || g_row[i] < nk)) dma16s(g_off[i], isv ? bv : bk, dst);
       }
     }
     t0_c += kBN;
-    if (t0_c >= S) { t0_c = 0; ++kf_c; }
+    fk += tile_bytes;
+    fv += tile_bytes;
+    if (t0_c >= S) {
+      t0_c = 0;
+      ++kf_c;
+      const int slot = (int)((pslots >> (4 * (kf_c - 1))) & 15);
+      const int64_t off = pbase + (int64_t)slot * S * tok_stride * 2;
+      fk = sp_k + off;
+      fv = sp_v + off;
+    }
     st_c = st_c == kStages - 1 ? 0 : st_c + 1;
   };
   // wait until this wavefront's copies of the oldest outstanding tile are done
   // while `ahead` younger tiles stay in flight (exact counts need full tiles)
   auto wait_tiles = [&](int ahead) {
-    if (FULL && ahead == 2) {
-      if (n_mine == C::MAXI) wait_vmcnt<2 * C::MAXI>(); else wait_vmcnt<2 * (C::MAXI - 1)>();
-    } else if (FULL && ahead == 1) {
-      if (n_mine == C::MAXI) wait_vmcnt<C::MAXI>(); else wait_vmcnt<C::MAXI - 1>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    if (!FULL) wait_vmcnt<0>();
+    else if (n_mine == MAXI) wait_vmcnt_tiles<MAXI>(ahead);
+    else wait_vmcnt_tiles<MAXI - 1>(ahead);
   };
 
   f32x16 acc[QB][DBLK];
@@ -323,6 +369,8 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
       }
     }
   };
+  // V^T operand of lane (g16, j16): dims 32i + 16(g16&1) + 4(j16&3) .. +3 of
+  // keys 16mm + 4(g16>>1) + (j16>>2) (+8 for the upper half), by transposing reads
   const int g16 = lane >> 4, j16 = lane & 15;
   auto pv = [&](const unsigned char* vs, int kb, const bf16x8v (&pf)[QB][2]) {
 #pragma unroll
@@ -342,11 +390,10 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
   };
 
-  // ---- prologue: tile 0 copied while Q is loaded, tiles 1..2 in flight, first chunk scored ----
+  // ---- prologue: tile 0 copied while Q is loaded, tiles 1..kStages-2 in flight, first chunk scored ----
   issue_next();
   wait_vmcnt<0>();   // Q and this wavefront's copies of tile 0 (the loop's waits count copies only)
-  if (n_tiles > 1) issue_next();
-  if (n_tiles > 2) issue_next();
+  for (int t = 1; t <= kStages - 2 && t < n_tiles; ++t) issue_next();
   lds_barrier();
   f32x16 s0[QB], s1[QB];
   bf16x8v pf[QB][2];
@@ -367,9 +414,9 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
     if (!FULL && nk_t < kBN) mask_tail(s1, 1, nk_t);
     max_rescale(s1);
     st_r = st_r == kStages - 1 ? 0 : st_r + 1;
-    wait_tiles(t + 2 < n_tiles ? 1 : 0);   // tile t+1 (t+2 may stay in flight)
-    lds_barrier();                          // every wavefront is done with tile t-1
-    if (t + 3 < n_tiles) issue_next();      // tile t+3 into tile t-1's stage
+    wait_tiles(min(kStages - 3, n_tiles - t - 2));   // tile t+1; younger tiles stay in flight
+    lds_barrier();                                    // every wavefront is done with tile t-1
+    if (t + kStages - 1 < n_tiles) issue_next();      // into tile t-1's stage
     // chunk 2t+2 (next tile) is scored while chunk 2t+1 is exponentiated
     qk(smem + st_r * C::STAGE, 0, s0);
     expc(s1, pf);
@@ -492,15 +539,15 @@ __global__ __launch_bounds__(64) void spatial_attn_f32_kernel(SpatialArgs a) {
   }
 }
 
-template <int D, int QB, int SW>
+template <int D, int QB, int SW, int ST>
 hipError_t launch_pipe_cfg(const SpatialArgs& a, hipStream_t s) {
   constexpr int BM = 32 * QB * SW;
   const int64_t nwg = (int64_t)((a.tokens + BM - 1) / BM) * a.n * a.heads * a.batch;
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
   if (a.tokens % kBN == 0)
-    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, true>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
+    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, true, ST>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
   else
-    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, false>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
+    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, false, ST>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -508,16 +555,17 @@ template <int D>
 hipError_t launch_mfma(const SpatialArgs& a, hipStream_t s) {
   // 64 queries per wavefront (each K/V operand read from LDS feeds two MFMAs)
   // once the grid has at least ~4 such workgroups per CU; 32 per wavefront
-  // below that, which doubles the number of wavefronts in flight.
-  // CA2_SPATIAL_QB=1|2 forces either.
+  // below that, which doubles the wavefronts in flight. Both with a 4-stage
+  // ring (two workgroups per CU for d <= 72).
+  // CA2_SPATIAL_CFG=1|2 forces 32 or 64 queries per wavefront.
   const int64_t frames = (int64_t)a.n * a.heads * a.batch;
   const int64_t wg_big = (int64_t)((a.tokens + 255) / 256) * frames;
-  int qb = wg_big >= 1024 ? 2 : 1;
-  if (const char* force = getenv("CA2_SPATIAL_QB")) qb = force[0] - '0';
+  int cfg = wg_big >= 1024 ? 2 : 1;
+  if (const char* force = getenv("CA2_SPATIAL_CFG")) cfg = force[0] - '0';
   if constexpr (D <= 72) {
-    if (qb == 2) return launch_pipe_cfg<D, 2, 4>(a, s);
+    if (cfg == 2) return launch_pipe_cfg<D, 2, 4, 4>(a, s);
   }
-  return launch_pipe_cfg<D, 1, 4>(a, s);
+  return launch_pipe_cfg<D, 1, 4, 4>(a, s);
 }
 
 template <int D>

@@ -185,19 +185,19 @@ def test_large_b8_s1024_sampled(ca2):
         check_close(to_host(os_)[b:b + 1, :, toks], ref_s, "bf16", f"large spatial b={b}")
 
 
-@pytest.mark.parametrize("qb", ["1", "2"])
+@pytest.mark.parametrize("cfg", ["1", "2"])
 @pytest.mark.parametrize("name,sh,writes,n,mode", [c for c in SPATIAL_CASES if c[1]["dtype"] == "bf16"],
                          ids=[c[0] for c in SPATIAL_CASES if c[1]["dtype"] == "bf16"])
-def test_spatial_parity_every_launch_variant(ca2, monkeypatch, qb, name, sh, writes, n, mode):
+def test_spatial_parity_every_launch_variant(ca2, monkeypatch, cfg, name, sh, writes, n, mode):
     """Both bf16 launch variants (4 wavefronts x 32 queries, 4 x 64 queries)
     against the oracle, whatever the grid size would pick."""
-    if qb == "2" and sh["d"] > 72:
+    if cfg == "2" and sh["d"] > 72:
         pytest.skip("64-query wavefronts are built for d <= 72 only")
-    monkeypatch.setenv("CA2_SPATIAL_QB", qb)
+    monkeypatch.setenv("CA2_SPATIAL_CFG", cfg)
     cache, o = fill(ca2, sh, 300, writes)
     q, k, v = (o.noisy(x, 2, 4, n) for x in ("q", "k", "v"))
     out = empty_like_dev(q.shape, "bf16")
     cache.ca2_spatial_attn(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), out, mode=mode)
     torch.cuda.synchronize()
     ref = o.spatial_out(q, k, v, "prefix" if mode == 0 else "self")
-    check_close(to_host(out), ref, "bf16", f"{name} qb {qb}")
+    check_close(to_host(out), ref, "bf16", f"{name} cfg {cfg}")
