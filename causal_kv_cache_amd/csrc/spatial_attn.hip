@@ -183,9 +183,11 @@ __device__ __forceinline__ void dma16s(unsigned voff, uint64_t sbase, unsigned l
                : "memory", "m0");
 }
 
-template <int D, int QB, int kSW, bool FULL, int kStages>
+template <int D, int QB, int kSW, bool FULL, int kStages, int KS>
 __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))) void spatial_attn_pipe_kernel(SpatialArgs a) {
   using C = SCfg<D, kSW>;
+  static_assert(KS == 1 || KS == 2, "key split over one or two wavefronts");
+  constexpr int G = kSW / KS;                      // query groups of 32*QB per workgroup
   static_assert(kStages >= 3, "the pipeline reads tile t+1 while tile t+2 is copied");
   constexpr int KSTEPS = C::KSTEPS, DBLK = C::DBLK, KSL = C::KSL, VSL = C::VSL, CH = C::CH;
   constexpr int MAXI = C::MAXI;                    // copies per wavefront per tile (upper bound)
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
   const int half = lane >> 5;
   const int col = lane & 31;
   const int S = a.tokens;
-  const int nq = (S + 32 * QB * kSW - 1) / (32 * QB * kSW);
+  const int nq = (S + 32 * QB * G - 1) / (32 * QB * G);
   const int w = xcd_work_index(blockIdx.x, gridDim.x);
   const int qblk = w % nq;
   const int f = (w / nq) % a.n;
@@ -205,7 +207,9 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
   const int b = w / (nq * a.n * a.heads);
   const int64_t tok_stride = (int64_t)a.heads * D;
   const int64_t own_off = (((int64_t)b * a.n + f) * S) * tok_stride + (int64_t)head * D;
-  const int q_base = qblk * (32 * QB * kSW) + wave * (32 * QB);
+  const int grp = wave % G;                        // query group of this wavefront
+  const int kh = wave / G;                         // with KS == 2: key half of every tile
+  const int q_base = qblk * (32 * QB * G) + grp * (32 * QB);
 
   bf16x8v qop[QB][KSTEPS];
   bool q_ok[QB];
@@ -224,22 +228,36 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
   }
   const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
   // Padding slots and the bytes past the last K / V row are never copied:
-  // write them once. Partial tiles also leave key rows uncopied, so without
-  // full tiles the whole ring starts zeroed.
-  for (int i = tid; i < kStages * C::STAGE / 16; i += 64 * kSW) {
-    const int off = (i * 16) % C::STAGE;
-    bool pad, ones = false;
-    if (off < C::V_OFF) {
-      const int r = off / C::KROW, c = (off % C::KROW) / 16;
-      pad = r >= kBN || c >= CH;
-    } else {
-      const int o = off - C::V_OFF, r = o / C::VROW, c = (o % C::VROW) / 16;
-      pad = r >= kBN || c >= CH;
-      ones = C::ONES && r < kBN && c == CH;
-    }
-    if (!FULL || pad) reinterpret_cast<uint4*>(smem)[i] = make_uint4(ones ? 0x3F80u : 0u, 0, 0, 0);
+  // write them once (the V slot at dim d holds the 1.0 of the row-sum trick).
+  // Partial tiles also leave key rows uncopied, so without full tiles the
+  // whole ring starts zeroed.
+  if constexpr (!FULL) {
+    for (int i = tid; i < kStages * C::STAGE / 16; i += 64 * kSW)
+      reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
   }
-  if constexpr (!FULL) __syncthreads();   // zeros land before any copy
+  {
+    constexpr int KP = KSL - CH, VP = VSL - CH;           // padding slots per row
+    constexpr int PER = kBN * (KP + VP) + 6;              // + 32 B after K, 64 B after V
+    for (int i = tid; i < kStages * PER; i += 64 * kSW) {
+      const int st = i / PER, k = i % PER;
+      int off;
+      bool ones = false;
+      if (KP > 0 && k < kBN * KP) {
+        constexpr int kp = KP > 0 ? KP : 1;
+        off = (k / kp) * C::KROW + (CH + k % kp) * 16;
+      } else if (k < kBN * (KP + VP)) {
+        const int kv = k - kBN * KP, c = CH + kv % VP;
+        off = C::V_OFF + (kv / VP) * C::VROW + c * 16;
+        ones = C::ONES && c == CH;
+      } else {
+        const int e = k - kBN * (KP + VP);
+        off = e < 2 ? kBN * C::KROW + 16 * e : C::V_OFF + kBN * C::VROW + 16 * (e - 2);
+      }
+      *reinterpret_cast<uint4*>(smem + st * C::STAGE + off) = make_uint4(ones ? 0x3F80u : 0u, 0, 0, 0);
+    }
+  }
+  if constexpr (!FULL) __syncthreads();   // ones land before any copy into the zeroed ring
   // copy stream: per-lane byte offsets of each of this wavefront's copy
   // instructions from the tile base (tile-independent), padding lanes masked
   const int n_mine = (C::NI - wave + kSW - 1) / kSW;
@@ -398,44 +416,106 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
   f32x16 s0[QB], s1[QB];
   bf16x8v pf[QB][2];
   int nk_t = min(kBN, S);             // keys in tile t
-  qk(smem, 0, s0);
-  if (!FULL && nk_t < 32) mask_tail(s0, 0, nk_t);
+  qk(smem, KS == 2 ? kh : 0, s0);
+  if (!FULL && nk_t < (KS == 2 ? kBN : 32)) mask_tail(s0, KS == 2 ? kh : 0, nk_t);
   max_rescale(s0);
 
   int st_r = 0;                       // stage of tile t
   int t0_n = kBN >= S ? 0 : kBN;      // first key of tile t+1 within its frame
-  for (int t = 0; t + 1 < n_tiles; ++t) {
-    const unsigned char* ks = smem + st_r * C::STAGE;
-    const unsigned char* vs = ks + C::V_OFF;
-    // chunk 2t+1 (same tile) is scored while chunk 2t is exponentiated
-    qk(ks, 1, s1);
-    expc(s0, pf);
-    pv(vs, 0, pf);
-    if (!FULL && nk_t < kBN) mask_tail(s1, 1, nk_t);
-    max_rescale(s1);
-    st_r = st_r == kStages - 1 ? 0 : st_r + 1;
-    wait_tiles(min(kStages - 3, n_tiles - t - 2));   // tile t+1; younger tiles stay in flight
-    lds_barrier();                                    // every wavefront is done with tile t-1
-    if (t + kStages - 1 < n_tiles) issue_next();      // into tile t-1's stage
-    // chunk 2t+2 (next tile) is scored while chunk 2t+1 is exponentiated
-    qk(smem + st_r * C::STAGE, 0, s0);
-    expc(s1, pf);
-    pv(vs, 1, pf);
-    nk_t = min(kBN, S - t0_n);
-    if (!FULL && nk_t < 32) mask_tail(s0, 0, nk_t);
-    max_rescale(s0);
-    t0_n = t0_n + kBN >= S ? 0 : t0_n + kBN;
-  }
-  {  // last tile
-    const unsigned char* ks = smem + st_r * C::STAGE;
-    const unsigned char* vs = ks + C::V_OFF;
-    qk(ks, 1, s1);
-    expc(s0, pf);
-    pv(vs, 0, pf);
-    if (!FULL && nk_t < kBN) mask_tail(s1, 1, nk_t);
-    max_rescale(s1);
-    expc(s1, pf);
-    pv(vs, 1, pf);
+  if constexpr (KS == 1) {
+    for (int t = 0; t + 1 < n_tiles; ++t) {
+      const unsigned char* ks = smem + st_r * C::STAGE;
+      const unsigned char* vs = ks + C::V_OFF;
+      // chunk 2t+1 (same tile) is scored while chunk 2t is exponentiated
+      qk(ks, 1, s1);
+      expc(s0, pf);
+      pv(vs, 0, pf);
+      if (!FULL && nk_t < kBN) mask_tail(s1, 1, nk_t);
+      max_rescale(s1);
+      st_r = st_r == kStages - 1 ? 0 : st_r + 1;
+      wait_tiles(min(kStages - 3, n_tiles - t - 2));   // tile t+1; younger tiles stay in flight
+      lds_barrier();                                    // every wavefront is done with tile t-1
+      if (t + kStages - 1 < n_tiles) issue_next();      // into tile t-1's stage
+      // chunk 2t+2 (next tile) is scored while chunk 2t+1 is exponentiated
+      qk(smem + st_r * C::STAGE, 0, s0);
+      expc(s1, pf);
+      pv(vs, 1, pf);
+      nk_t = min(kBN, S - t0_n);
+      if (!FULL && nk_t < 32) mask_tail(s0, 0, nk_t);
+      max_rescale(s0);
+      t0_n = t0_n + kBN >= S ? 0 : t0_n + kBN;
+    }
+    {  // last tile
+      const unsigned char* ks = smem + st_r * C::STAGE;
+      const unsigned char* vs = ks + C::V_OFF;
+      qk(ks, 1, s1);
+      expc(s0, pf);
+      pv(vs, 0, pf);
+      if (!FULL && nk_t < kBN) mask_tail(s1, 1, nk_t);
+      max_rescale(s1);
+      expc(s1, pf);
+      pv(vs, 1, pf);
+    }
+  } else {
+    // one chunk (key half kh) per tile: this wavefront's chunk of tile t+1 is
+    // scored while its chunk of tile t is exponentiated and accumulated
+    auto step = [&](f32x16 (&sa)[QB], f32x16 (&sb)[QB], int t) {
+      const unsigned char* vs = smem + st_r * C::STAGE + C::V_OFF;
+      st_r = st_r == kStages - 1 ? 0 : st_r + 1;
+      wait_tiles(min(kStages - 3, n_tiles - t - 2));   // tile t+1; younger tiles stay in flight
+      lds_barrier();                                    // every wavefront is done with tile t-1
+      if (t + kStages - 1 < n_tiles) issue_next();      // into tile t-1's stage
+      qk(smem + st_r * C::STAGE, kh, sb);
+      expc(sa, pf);
+      pv(vs, kh, pf);
+      nk_t = min(kBN, S - t0_n);
+      if (!FULL && nk_t < kBN) mask_tail(sb, kh, nk_t);
+      max_rescale(sb);
+      t0_n = t0_n + kBN >= S ? 0 : t0_n + kBN;
+    };
+    auto last = [&](const f32x16 (&sa)[QB]) {
+      expc(sa, pf);
+      pv(smem + st_r * C::STAGE + C::V_OFF, kh, pf);
+    };
+    for (int t = 0;; t += 2) {
+      if (t + 1 >= n_tiles) { last(s0); break; }
+      step(s0, s1, t);
+      if (t + 2 >= n_tiles) { last(s1); break; }
+      step(s1, s0, t + 1);
+    }
+    // merge the two key halves (flash attention partial states combine by
+    // rescaling to the larger running maximum): half 1 hands over to half 0
+    constexpr int PER = QB * (DBLK * 16 + 2);         // floats per lane
+    static_assert(G * 64 * PER * 4 <= kStages * C::STAGE, "merge area");
+    lds_barrier();                                    // the ring is no longer read
+    float* mg = reinterpret_cast<float*>(smem) + grp * 64 * PER;
+    if (kh == 1) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float* d = mg + qb * (DBLK * 16 + 2) * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) d[(i * 16 + r) * 64] = acc[qb][i][r];
+        d[(DBLK * 16) * 64] = m_run[qb];
+        d[(DBLK * 16 + 1) * 64] = l_run[qb];
+      }
+    }
+    lds_barrier();
+    if (kh == 1) return;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float* d = mg + qb * (DBLK * 16 + 2) * 64 + lane;
+      const float m_o = d[(DBLK * 16) * 64];
+      const float m_new = __builtin_fmaxf(m_run[qb], m_o);
+      const float c_me = fast_exp2(m_run[qb] - m_new), c_o = fast_exp2(m_o - m_new);
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[qb][i][r] = acc[qb][i][r] * c_me + d[(i * 16 + r) * 64] * c_o;
+      l_run[qb] = l_run[qb] * c_me + d[(DBLK * 16 + 1) * 64] * c_o;
+      m_run[qb] = m_new;
+    }
   }
 
 #pragma unroll
@@ -539,33 +619,36 @@ __global__ __launch_bounds__(64) void spatial_attn_f32_kernel(SpatialArgs a) {
   }
 }
 
-template <int D, int QB, int SW, int ST>
+template <int D, int QB, int SW, int ST, int KS>
 hipError_t launch_pipe_cfg(const SpatialArgs& a, hipStream_t s) {
-  constexpr int BM = 32 * QB * SW;
+  constexpr int BM = 32 * QB * SW / KS;
   const int64_t nwg = (int64_t)((a.tokens + BM - 1) / BM) * a.n * a.heads * a.batch;
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
   if (a.tokens % kBN == 0)
-    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, true, ST>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
+    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, true, ST, KS>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
   else
-    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, false, ST>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
+    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, false, ST, KS>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_mfma(const SpatialArgs& a, hipStream_t s) {
-  // 64 queries per wavefront (each K/V operand read from LDS feeds two MFMAs)
-  // once the grid has at least ~4 such workgroups per CU; 32 per wavefront
-  // below that, which doubles the wavefronts in flight. Both with a 4-stage
-  // ring (two workgroups per CU for d <= 72).
-  // CA2_SPATIAL_CFG=1|2 forces 32 or 64 queries per wavefront.
+  // Large grids: 4 wavefronts x 64 queries (each K/V operand read from LDS
+  // feeds two MFMAs), two workgroups per CU. Below ~4 such workgroups per CU:
+  // 4 x 32 queries, which doubles the wavefronts in flight.
+  // CA2_SPATIAL_CFG=1|2|3 forces 32 queries, 64 queries, or 8 wavefronts of
+  // 32 queries x 2 key halves (two wavefronts per SIMD even at one workgroup
+  // per CU; measured slower than 4 x 32 at the 256-token shape, kept
+  // selectable).
   const int64_t frames = (int64_t)a.n * a.heads * a.batch;
   const int64_t wg_big = (int64_t)((a.tokens + 255) / 256) * frames;
   int cfg = wg_big >= 1024 ? 2 : 1;
   if (const char* force = getenv("CA2_SPATIAL_CFG")) cfg = force[0] - '0';
   if constexpr (D <= 72) {
-    if (cfg == 2) return launch_pipe_cfg<D, 2, 4, 4>(a, s);
+    if (cfg == 2) return launch_pipe_cfg<D, 2, 4, 4, 1>(a, s);
   }
-  return launch_pipe_cfg<D, 1, 4, 4>(a, s);
+  if (cfg == 3) return launch_pipe_cfg<D, 1, 8, 4, 2>(a, s);
+  return launch_pipe_cfg<D, 1, 4, 4, 1>(a, s);
 }
 
 template <int D>

@@ -185,12 +185,13 @@ def test_large_b8_s1024_sampled(ca2):
         check_close(to_host(os_)[b:b + 1, :, toks], ref_s, "bf16", f"large spatial b={b}")
 
 
-@pytest.mark.parametrize("cfg", ["1", "2"])
+@pytest.mark.parametrize("cfg", ["1", "2", "3"])
 @pytest.mark.parametrize("name,sh,writes,n,mode", [c for c in SPATIAL_CASES if c[1]["dtype"] == "bf16"],
                          ids=[c[0] for c in SPATIAL_CASES if c[1]["dtype"] == "bf16"])
 def test_spatial_parity_every_launch_variant(ca2, monkeypatch, cfg, name, sh, writes, n, mode):
-    """Both bf16 launch variants (4 wavefronts x 32 queries, 4 x 64 queries)
-    against the oracle, whatever the grid size would pick."""
+    """Every bf16 launch variant (4 wavefronts x 32 queries, 4 x 64 queries,
+    8 wavefronts = 4 x 32 queries x 2 key halves) against the oracle,
+    whatever the grid size would pick."""
     if cfg == "2" and sh["d"] > 72:
         pytest.skip("64-query wavefronts are built for d <= 72 only")
     monkeypatch.setenv("CA2_SPATIAL_CFG", cfg)
