@@ -55,4 +55,40 @@ template <> struct Elem<bf16_t> {
   }
 };
 
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt vmcnt(ahead * per) for a wave-uniform ahead in [0, kMax]; the
+// count must be an immediate, so each value gets its own instruction.
+template <int per, int k = 0, int kMax = 8>
+__device__ __forceinline__ void wait_vmcnt_tiles(int ahead) {
+  if constexpr (k > kMax || k * per > 63) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead == k) wait_vmcnt<k * per>();
+    else wait_vmcnt_tiles<per, k + 1, kMax>(ahead);
+  }
+}
+
+// A wavefront-uniform 64-bit value as such (readfirstlane returns int: widen
+// through unsigned, never sign-extend).
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v >> 32));
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
+// 16-byte global -> LDS copy for every active lane: lane i reads
+// sbase + voff (+ 0..15) and writes lds_addr + 16*i (lds_addr in M0);
+// sbase and lds_addr are wavefront-uniform.
+__device__ __forceinline__ void dma16s(unsigned voff, uint64_t sbase, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(uniform64(sbase)), "s"((unsigned)__builtin_amdgcn_readfirstlane((int)lds_addr))
+               : "memory", "m0");
+}
+
 }  // namespace ca2

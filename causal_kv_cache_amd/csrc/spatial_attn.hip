@@ -78,33 +78,6 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
-// 16-byte global -> LDS copy for every active lane: lane i writes
-// lds_addr + 16*i (lds_addr is wavefront-uniform, held in M0). The copy has
-// no register result; completion is tracked by vmcnt.
-__device__ __forceinline__ void dma16(const void* gptr, unsigned lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// s_waitcnt vmcnt(ahead * per) for a wave-uniform ahead in [0, kMax]; the
-// count must be an immediate, so each value gets its own instruction.
-template <int per, int k = 0, int kMax = 8>
-__device__ __forceinline__ void wait_vmcnt_tiles(int ahead) {
-  if constexpr (k > kMax || k * per > 63) {
-    wait_vmcnt<0>();
-  } else {
-    if (ahead == k) wait_vmcnt<k * per>();
-    else wait_vmcnt_tiles<per, k + 1, kMax>(ahead);
-  }
-}
-
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -165,23 +138,6 @@ __device__ __forceinline__ void lazy_rescale(float mx, float& m_run, float& l_ru
 // scored during tile t, so tile t+1 must be resident one iteration early: at
 // iteration t a wavefront waits for its copies of tile t+1 and, after the
 // barrier, refills the stage of tile t-1 with tile t+kStages-1.
-
-// A wavefront-uniform 64-bit value as such (readfirstlane returns int: widen
-// through unsigned, never sign-extend).
-__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
-  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
-  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v >> 32));
-  return ((uint64_t)hi << 32) | (uint64_t)lo;
-}
-
-// 16-byte global -> LDS copy for every active lane: lane i reads
-// sbase + voff (+ 0..15) and writes lds_addr + 16*i (lds_addr in M0);
-// sbase and lds_addr are wavefront-uniform.
-__device__ __forceinline__ void dma16s(unsigned voff, uint64_t sbase, unsigned lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(uniform64(sbase)), "s"((unsigned)__builtin_amdgcn_readfirstlane((int)lds_addr))
-               : "memory", "m0");
-}
 
 template <int D, int QB, int kSW, bool FULL, int kStages, int KS>
 __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))) void spatial_attn_pipe_kernel(SpatialArgs a) {
