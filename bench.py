@@ -204,9 +204,16 @@ SOURCES = {"spatial_prefix": "spatial_attn.hip", "spatial_self": "spatial_attn.h
 
 
 def source_hash(kernel):
+    """Hash of the kernel's source code with comments and whitespace removed
+    (a comment edit does not invalidate recorded counters)."""
+    import re
     p = os.path.join(ROOT, "causal_kv_cache_amd", "csrc", SOURCES[kernel])
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(p) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    src = re.sub(r"\s+", "", src)
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def traffic_for(kernel, workload):

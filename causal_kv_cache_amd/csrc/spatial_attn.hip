@@ -7,17 +7,16 @@
 // one-chunk spatial KV buffer.
 //
 // bf16 path = flash attention on MFMA (v_mfma_f32_32x32x16_bf16):
-//   * workgroup = 4 wavefronts x 32 queries of one (b, frame, head);
-//   * key tiles of 64 keys are staged in LDS: K row-major (row stride d*2
-//     bytes: 16-byte reads by 8 consecutive rows hit distinct banks), V
-//     transposed (V^T[dim][key], row stride 136 bytes) while staging;
-//   * per tile each wavefront computes S^T = K Q^T (keys x queries) so a lane
-//     owns one query column: the softmax row statistics are per lane, shared
-//     with the partner lane (lane ^ 32) by one exchange, and the exponentiated
-//     scores are already laid out as the B operand of O^T = V^T P^T -- they
-//     never leave registers;
+//   * a workgroup covers 4 wavefronts x 32*QB queries of one (b, frame, head);
+//   * per key tile each wavefront computes S^T = K Q^T (keys x queries) so a
+//     lane owns one query column: the softmax row statistics are per lane,
+//     shared with the partner lane (lane ^ 32) by one exchange, and the
+//     exponentiated scores are already laid out as the B operand of
+//     O^T = V^T P^T -- they never leave registers;
 //   * online softmax in base 2 (scale * log2 e folded into one FMA), fp32
-//     statistics, P rounded to bf16 for the PV product, fp32 accumulators.
+//     statistics, P rounded to bf16 for the PV product, fp32 accumulators;
+//     the V row padding holds 1.0 at dim d, so row d of O^T is the softmax
+//     normaliser, computed by the MFMA from the same bf16 P as the numerator.
 // The fp32 path (for fp32 caches) is a plain LDS-tiled VALU kernel.
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -28,15 +27,8 @@ namespace ca2 {
 namespace {
 
 // ----------------------------------------------------------------------------
-// bf16 MFMA kernel
+// bf16 MFMA kernel: tile geometry and helpers
 // ----------------------------------------------------------------------------
-// Pipeline: key tiles of 64 keys stream through a 3-stage LDS ring. Each tile
-// is copied HBM -> LDS by global_load_lds_dwordx4 (asynchronous DMA, 16 bytes
-// per lane, no register staging) two tiles ahead of its use; a wavefront waits
-// only for its own copies of the tile it is about to read (s_waitcnt vmcnt),
-// then one barrier per tile publishes it to the workgroup. K and V stay
-// row-major in LDS; the V^T operand of the PV product is read with
-// ds_read_b64_tr_b16, which transposes 16-bit data across each 16-lane group.
 constexpr int kBN = 64;                  // keys per tile
 constexpr float kNoMax = -1.0e30f;       // running max before the first tile
 constexpr float kLazy = 8.0f;            // raise the running max only past this margin (base 2)
