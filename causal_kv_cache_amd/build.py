@@ -39,10 +39,17 @@ def flags() -> list:
     ]
 
 
+# Per-source flags. The spatial kernel takes maxima of MFMA results; under
+# IEEE NaN rules every such max is preceded by a canonicalising v_max (x, x),
+# 16 per key tile. NaN inputs still propagate through the MFMAs to the
+# output, and -inf (used for masking) is still honoured.
+SOURCE_FLAGS = {"spatial_attn.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + flags() + SOURCE_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -89,16 +89,20 @@ __device__ __forceinline__ int xcd_work_index(int block, int nblocks) {
 }
 
 // Lazy rescale of one query block's running state: only when a lane's new
-// maximum passes its running maximum by more than 2^kLazy. The test is made
-// wave-uniform so that the common case is one scalar branch; inside, lanes
-// that keep their maximum get a factor of exactly 1.
+// maximum passes its running maximum m by more than 2^kLazy (base 2). The
+// test runs on the raw score maximum against thr = (m + kLazy) / c, c =
+// scale * log2 e (kept with m, changed only here), and is made wave-uniform
+// so the common case is one compare and one scalar branch; inside, lanes that
+// keep their maximum get a factor of exactly 1.
 template <int DBLK>
-__device__ __forceinline__ void lazy_rescale(float mx, float& m_run, float& l_run, f32x16 (&acc)[DBLK]) {
-  const bool need = mx > m_run + kLazy;
+__device__ __forceinline__ void lazy_rescale(float mx_raw, float c, float& m_run, float& thr, float& l_run,
+                                             f32x16 (&acc)[DBLK]) {
+  const bool need = mx_raw > thr;
   if (__builtin_amdgcn_ballot_w64(need) == 0) return;
-  const float m_new = need ? mx : m_run;
+  const float m_new = need ? mx_raw * c : m_run;
   const float corr = fast_exp2(m_run - m_new);
   m_run = m_new;
+  thr = (m_new + kLazy) / c;
   l_run *= corr;
 #pragma unroll
   for (int i = 0; i < DBLK; ++i)
@@ -281,9 +285,9 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
     for (int i = 0; i < DBLK; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[qb][i][r] = 0.f;
-  float m_run[QB], l_run[QB];
+  float m_run[QB], l_run[QB], thr[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = kNoMax; l_run[qb] = 0.f; }
+  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = kNoMax; l_run[qb] = 0.f; thr[qb] = (kNoMax + kLazy) / a.scale_log2e; }
 
   const f32x16 zero16 = {};
   // S^T = K Q^T for keys kb*32 .. +31 of a tile: sc[qb] register r holds key
@@ -312,8 +316,7 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
       float mx = __builtin_fmaxf(sc[qb][0], sc[qb][1]);
 #pragma unroll
       for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[qb][r]), sc[qb][r + 1]);
-      mx = max_halves(mx) * a.scale_log2e;
-      lazy_rescale(mx, m_run[qb], l_run[qb], acc[qb]);
+      lazy_rescale(max_halves(mx), a.scale_log2e, m_run[qb], thr[qb], l_run[qb], acc[qb]);
     }
   };
   // P of one chunk as the B operands of two 16-key k-steps
