@@ -91,4 +91,13 @@ __device__ __forceinline__ void dma16s(unsigned voff, uint64_t sbase, unsigned l
                : "memory", "m0");
 }
 
+// Block index -> work index such that XCD x (which receives blocks x, x+8,
+// x+16, ...) processes work items [start_x, start_x + count_x) in order.
+__device__ __forceinline__ int xcd_work_index(int block, int nblocks) {
+  constexpr int kXcds = 8;
+  const int q = nblocks / kXcds, r = nblocks % kXcds;
+  const int x = block % kXcds, local = block / kXcds;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
+
 }  // namespace ca2

@@ -7,106 +7,142 @@
 // split into three [m][c] tensors in the activation layout the cache write
 // consumes.
 //
-// Tiling: workgroup tile 128 (output channels n) x 128 (tokens m), 4
-// wavefronts of 64 x 64, k-tile 64, v_mfma_f32_32x32x16_bf16. The product is
-// formed as C^T = W X^T so that a lane owns one token row and its 16
-// accumulator registers hold runs of 4 consecutive channels (8-byte stores).
-// LDS rows are 144 bytes (128 + 16 pad) so 8 consecutive rows read distinct
-// banks; the next k-tile is loaded into registers while the current one is
-// multiplied.
+// Tiling: workgroup tile 256 output channels (n) x 256 tokens (m), 8
+// wavefronts (two per SIMD) of 128 x 64 (4 x 2 v_mfma_f32_32x32x16_bf16
+// blocks, 128 accumulators per lane). The product is formed as C^T = W X^T so that a lane owns
+// one token row and its accumulator registers hold runs of 4 consecutive
+// channels (8-byte stores). k-tiles of 64 are double-buffered in LDS and
+// filled by global_load_lds_dwordx4 in its scalar-base form: an LDS row is
+// 144 bytes (128 of data + a 16-byte pad slot, so 8 consecutive rows read
+// distinct banks), copy instruction j covers 16-byte slots 64j..64j+63 of the
+// 256 rows, each lane's offset from the k-tile base is a constant, and the
+// pad lanes are masked. Within a k-tile the operands of k-step s+1 are read
+// from LDS into a second register set while the 16 MFMAs of k-step s run
+// (one wavefront per SIMD: nothing else would hide the LDS latency).
+// Workgroups are dealt so that each XCD takes a contiguous run of tiles
+// sharing token panels.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace ca2 {
 namespace {
 
-constexpr int TN = 128;   // output channels per workgroup
-constexpr int TM = 128;   // tokens per workgroup
-constexpr int TK = 64;    // contraction per step
-constexpr int LSTR = TK * 2 + 16;
-constexpr int kThreads = 256;
-constexpr int kLoads = (TN * TK / 8) / kThreads;   // 16-byte chunks per thread per operand (4)
+constexpr int TN = 256;                 // output channels per workgroup
+constexpr int TM = 256;                 // tokens per workgroup
+constexpr int TK = 64;                  // contraction per k-tile
+constexpr int kSlots = TK * 2 / 16 + 1; // 16-byte slots per LDS row (data + pad)
+constexpr int ROWB = kSlots * 16;       // 144
+constexpr int OPB = TN * ROWB;          // one operand tile
+constexpr int STAGE = 2 * OPB;          // W tile, then X tile
+constexpr int kStages = 2;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int NI = TN * kSlots / 64;    // copy instructions per operand per k-tile (36)
+constexpr int kPer = 2 * NI / kWaves;   // per wavefront per k-tile (9)
+static_assert(TN == TM && (TN * kSlots) % 64 == 0 && (2 * NI) % kWaves == 0, "copy geometry");
 
-__global__ __launch_bounds__(kThreads) void qkv_proj_kernel(ProjArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char sw[TN * LSTR];
-  __shared__ __attribute__((aligned(16))) unsigned char sx[TM * LSTR];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void qkv_proj_kernel(ProjArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * STAGE];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const int wn = wave & 1, wm = wave >> 1;
-  const int n0 = blockIdx.x * TN;
-  const int m0 = blockIdx.y * TM;
+  const int wn = wave & 1, wm = wave >> 1;       // 128 channels x 64 tokens per wavefront
   const int N = 3 * a.c_out;
-  const bf16_t* __restrict__ W = static_cast<const bf16_t*>(a.w);
-  const bf16_t* __restrict__ X = static_cast<const bf16_t*>(a.x);
+  const int tiles_n = (N + TN - 1) / TN;
+  const int w = xcd_work_index(blockIdx.x, gridDim.x);
+  const int n0 = (w % tiles_n) * TN;
+  const int m0 = (w / tiles_n) * TM;
+  const bool edge = n0 + TN > N || m0 + TM > a.m;   // rows past the matrices: masked copies
+  const int KT = a.c_in / TK;
 
-  f32x16 acc[2][2];
+  // per-lane copy offsets (bytes from the k-tile base) for this wavefront's
+  // instructions: j = wave + 4i over the W tile (j < NI) then the X tile
+  unsigned g_off[kPer];
+  bool g_ok[kPer];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kPer; ++i) {
+    const int j = wave + kWaves * i;
+    const bool isx = j >= NI;
+    const int slot = (isx ? j - NI : j) * 64 + lane;
+    const int row = slot / kSlots, c = slot % kSlots;
+    g_ok[i] = c < kSlots - 1 && (isx ? m0 + row < a.m : n0 + row < N);
+    g_off[i] = (unsigned)row * (unsigned)(a.c_in * 2) + 16u * c;
+  }
+  const uint64_t wbase = reinterpret_cast<uint64_t>(a.w) + (uint64_t)n0 * a.c_in * 2;
+  const uint64_t xbase = reinterpret_cast<uint64_t>(a.x) + (uint64_t)m0 * a.c_in * 2;
+  const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  auto issue = [&](int t) {                        // k-tile t into stage t % kStages
+    const unsigned st = lds_base + (t % kStages) * STAGE;
+    const uint64_t kb = (uint64_t)t * TK * 2;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int j = wave + kWaves * i;
+      const bool isx = j >= NI;
+      if (g_ok[i]) dma16s(g_off[i], (isx ? xbase : wbase) + kb, st + (isx ? OPB + (j - NI) * 1024 : j * 1024));
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 rw[kLoads], rx[kLoads];
-  auto load = [&](int k0) {
+  bf16x8v wa[2][4], xb[2][2];
+  auto load_ops = [&](const unsigned char* sw, int s, int buf) {
+    const unsigned char* sx = sw + OPB;
 #pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      const int e = u * kThreads + tid;
-      const int row = e >> 3, c = e & 7;
-      const int n = n0 + row, m = m0 + row;
-      rw[u] = n < N ? *reinterpret_cast<const uint4*>(W + (int64_t)n * a.c_in + k0 + c * 8)
-                    : make_uint4(0, 0, 0, 0);
-      rx[u] = m < a.m ? *reinterpret_cast<const uint4*>(X + (int64_t)m * a.c_in + k0 + c * 8)
-                      : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      wa[buf][i] = *reinterpret_cast<const bf16x8v*>(sw + (wn * 128 + i * 32 + col) * ROWB + (16 * s + 8 * half) * 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      xb[buf][j] = *reinterpret_cast<const bf16x8v*>(sx + (wm * 64 + j * 32 + col) * ROWB + (16 * s + 8 * half) * 2);
   };
-  load(0);
-  for (int k0 = 0; k0 < a.c_in; k0 += TK) {
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      const int e = u * kThreads + tid;
-      const int row = e >> 3, c = e & 7;
-      *reinterpret_cast<uint4*>(sw + row * LSTR + c * 16) = rw[u];
-      *reinterpret_cast<uint4*>(sx + row * LSTR + c * 16) = rx[u];
-    }
-    __syncthreads();
-    if (k0 + TK < a.c_in) load(k0 + TK);
+  issue(0);
+  for (int t = 0; t < KT; ++t) {
+    wait_vmcnt<0>();                               // this wavefront's copies of k-tile t
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();                  // k-tile t visible; stage of k-tile t-1 free
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (t + 1 < KT) issue(t + 1);
+    const unsigned char* sw = smem + (t % kStages) * STAGE;
+    load_ops(sw, 0, 0);
 #pragma unroll
     for (int s = 0; s < TK / 16; ++s) {
-      bf16x8v wa[2], xb[2];
+      // the reads of k-step s+1 are issued before the MFMAs of k-step s (the
+      // scheduling barriers keep the compiler from sinking them to their uses)
+      if (s + 1 < TK / 16) load_ops(sw, s + 1, (s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        wa[i] = *reinterpret_cast<const bf16x8v*>(sw + (wn * 64 + i * 32 + col) * LSTR + (16 * s + 8 * half) * 2);
-        xb[i] = *reinterpret_cast<const bf16x8v*>(sx + (wm * 64 + i * 32 + col) * LSTR + (16 * s + 8 * half) * 2);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[i], xb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[s & 1][i], xb[s & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // register r of acc[i][j]: channel n0 + wn*64 + 32i + 8(r/4) + 4*half + r%4,
+  // register r of acc[i][j]: channel n0 + wn*128 + 32i + 8(r/4) + 4*half + r%4,
   // token m0 + wm*64 + 32j + col
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int m = m0 + wm * 64 + 32 * j + col;
     if (m >= a.m) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 64 + 32 * i + 8 * g + 4 * half;
+        const int n = n0 + wn * 128 + 32 * i + 8 * g + 4 * half;
         if (n >= N) continue;
         const int seg = n / a.c_out;
         bf16_t* dst = static_cast<bf16_t*>(seg == 0 ? a.q : seg == 1 ? a.k : a.v);
-        uint2 w;
-        w.x = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-        w.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-        *reinterpret_cast<uint2*>(dst + (int64_t)m * a.c_out + (n - seg * a.c_out)) = w;
+        uint2 v;
+        v.x = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+        v.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        *reinterpret_cast<uint2*>(dst + (int64_t)m * a.c_out + (n - seg * a.c_out)) = v;
       }
   }
 }
@@ -115,8 +151,10 @@ __global__ __launch_bounds__(kThreads) void qkv_proj_kernel(ProjArgs a) {
 
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s) {
   if (a.m < 1 || a.c_in % TK || a.c_out % 64) return hipErrorInvalidValue;
-  const dim3 grid((3 * a.c_out + TN - 1) / TN, (a.m + TM - 1) / TM);
-  hipLaunchKernelGGL(qkv_proj_kernel, grid, dim3(kThreads), 0, s, a);
+  if ((int64_t)TN * a.c_in * 2 > 0xffffffffLL) return hipErrorInvalidValue;   // 32-bit copy offsets
+  const int64_t tiles = (int64_t)((3 * a.c_out + TN - 1) / TN) * ((a.m + TM - 1) / TM);
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(qkv_proj_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -79,14 +79,6 @@ __device__ __forceinline__ void lds_barrier() {
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
 
-// Block index -> work index such that XCD x (which receives blocks x, x+8,
-// x+16, ...) processes work items [start_x, start_x + count_x) in order.
-__device__ __forceinline__ int xcd_work_index(int block, int nblocks) {
-  constexpr int kXcds = 8;
-  const int q = nblocks / kXcds, r = nblocks % kXcds;
-  const int x = block % kXcds, local = block / kXcds;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
-}
 
 // Lazy rescale of one query block's running state: only when a lane's new
 // maximum passes its running maximum m by more than 2^kLazy (base 2). The
