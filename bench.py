@@ -156,6 +156,29 @@ def time_launches(fn, reps):
     return e0.elapsed_time(e1) * 1e3 / reps     # microseconds
 
 
+def denoise_loop_graph(w: Workload, reps: int):
+    """The 50 denoising calls of one AR step (they share one state of each
+    cache) launched eagerly and as one captured HIP graph: average ms per loop.
+    The cache-writing pass changes the queue and cannot be replayed, so the
+    headline step launches eagerly; this only reports the difference."""
+    import torch
+
+    def loop():
+        for t in range(T_DENOISE):
+            w.denoise(t)
+
+    eager = time_launches(loop, reps) / 1e3
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        loop()
+    torch.cuda.synchronize()
+    graph = time_launches(g.replay, reps) / 1e3
+    del g
+    return eager, graph
+
+
 def kernel_table(w: Workload, reps: int):
     """Per-kernel average launch duration and roofline numbers for one workload."""
     from causal_kv_cache_amd import ca2
@@ -354,6 +377,7 @@ def main():
     tokens = args.steps * T_DENOISE * AR_STEP["B"] * AR_STEP["l"] * AR_STEP["S"]
     value = tokens / wall
 
+    loop_eager, loop_graph = denoise_loop_graph(w, 10)
     kt = kernel_table(w, args.kernel_reps)
     # dominant kernel of the step: largest total time per step
     per_step = {"spatial_attn_prefix": T_DENOISE * kt["spatial_attn_prefix"]["us"],
@@ -377,6 +401,7 @@ def main():
         "config": {"workload": AR_STEP["name"], "batch": 1, "heads": 16, "head_dim": 72, "tokens": 256,
                    "chunk": 8, "p_max": 25, "p_k": 25, "p_spatial": 3, "denoise_calls_per_step": T_DENOISE},
         "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
+        "denoise_loop_50_calls_ms": {"eager": round(loop_eager, 4), "hip_graph_replay": round(loop_graph, 4)},
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r.items()}
                     for k, r in kt.items()},
