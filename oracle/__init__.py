@@ -29,6 +29,7 @@ from .attention import (
     spatial_attn_selfrepeat_ref,
     masked_causal_attn_ref,
     full_recompute_temporal_ref,
+    bidirectional_temporal_ref,
 )
 from .cache import (
     TemporalQueue,
@@ -42,7 +43,7 @@ from .rollout import ar_schedule, RolloutOracle
 __all__ = [
     "softmax_rows", "temporal_attn_ref", "spatial_attn_ref",
     "spatial_attn_selfrepeat_ref", "masked_causal_attn_ref",
-    "full_recompute_temporal_ref", "TemporalQueue", "SpatialCache",
+    "full_recompute_temporal_ref", "bidirectional_temporal_ref", "TemporalQueue", "SpatialCache",
     "tpe_index_ref", "bytes_resident_ref", "qkv_proj_ref", "ar_schedule",
     "RolloutOracle",
 ]

@@ -198,3 +198,29 @@ def full_recompute_temporal_ref(q_chunk, k_seq, v_seq, n0, p_max, scale):
                 out[b, :, s, h] = masked_causal_attn_ref(
                     q_chunk[b, :, s, h], k_seq[b, :, s, h], v_seq[b, :, s, h], M, scale)
     return out
+
+
+def bidirectional_temporal_ref(q, k, v, scale):
+    """Temporal attention without a cache: every frame attends to every frame.
+
+    This is the recompute baseline the Ca2-VDM pages measure against (the
+    abstract page and the notes' speed comparison: existing VDMs attend
+    bidirectionally along time, so the conditional frames' K/V depend on the
+    noisy frames and are recomputed at every denoising step; OS-Ext extends the
+    conditioning and its time grows quadratically with the autoregression
+    step). For each row (b, s, h), query frame i in [0, T) attends to all T
+    frames with no mask: Softmax(scale * Q K^T) V over the frame axis.
+
+    q, k, v: [B][T][S][H][d]. Returns float64 [B][T][S][H][d].
+
+    Pinned by: permutation equivariance over frames, the last frame equal to
+    the causal oracle's last frame, the K == 0 closed form, brute force through
+    ``masked_causal_attn_ref`` with an all-zero mask, and torch's unmasked SDPA
+    (tests/test_oracle_attention.py).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    z = scale * np.einsum("btshd,bjshd->bshtj", q, k)
+    p = softmax_rows(z)
+    return np.einsum("bshtj,bjshd->btshd", p, v)

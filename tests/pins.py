@@ -163,3 +163,56 @@ def check_spatial_zero_query(spatial_impl, B=1, n=2, S=6, H=2, d=4, p=3, seed=5)
         mean = (v[:, f].sum(1) + vs.sum((1, 2))) / ((p + 1) * S)          # [B][H][d]
         worst = max(worst, float(np.max(np.abs(got[:, f] - mean[:, None]))))
     return worst
+
+
+# ---------------------------------------------------------------------------
+# bidirectional temporal attention (the recompute baseline)
+# ---------------------------------------------------------------------------
+def check_bidirectional_vs_sdpa(bidir_impl, B=2, T=6, S=3, H=2, d=8, seed=11):
+    """Every frame attends to every frame: torch's unmasked SDPA along frames."""
+    g = np.random.default_rng(seed)
+    q, k, v = (g.standard_normal((B, T, S, H, d)) for _ in range(3))
+    scale = 0.37
+    got = bidir_impl(q, k, v, scale)
+    perm = (0, 2, 3, 1, 4)
+    ref = sdpa64(q.transpose(perm), k.transpose(perm), v.transpose(perm), scale)
+    return float(np.max(np.abs(got.transpose(perm) - ref)))
+
+
+def check_bidirectional_zero_keys(bidir_impl, B=1, T=5, S=2, H=3, d=4, seed=12):
+    """K == 0: every logit equal, so every query frame returns the mean of the
+    values over all T frames (one-hot frame codes make any left-out or
+    doubled frame visible)."""
+    g = np.random.default_rng(seed)
+    q = g.standard_normal((B, T, S, H, d))
+    k = np.zeros((B, T, S, H, d))
+    v = np.zeros((B, T, S, H, T))
+    for t in range(T):
+        v[:, t, ..., t] = 1.0
+    got = bidir_impl(q, k, v, 0.5)
+    return float(np.max(np.abs(got - 1.0 / T)))
+
+
+def check_bidirectional_permutation(bidir_impl, B=1, T=7, S=2, H=2, d=6, seed=13):
+    """Permuting the frames of q, k and v permutes the output the same way;
+    permuting only the key/value frames (together) leaves it unchanged."""
+    g = np.random.default_rng(seed)
+    q, k, v = (g.standard_normal((B, T, S, H, d)) for _ in range(3))
+    perm = g.permutation(T)
+    base = bidir_impl(q, k, v, 0.3)
+    a = bidir_impl(q[:, perm], k[:, perm], v[:, perm], 0.3)
+    b = bidir_impl(q, k[:, perm], v[:, perm], 0.3)
+    return float(max(np.max(np.abs(a - base[:, perm])), np.max(np.abs(b - base))))
+
+
+def check_bidirectional_last_frame_is_causal(bidir_impl, causal_impl, B=1, T=6, S=3, H=2, d=8, seed=14):
+    """The last frame sees all frames under the causal mask as well, so it
+    matches the causal temporal oracle (empty queue) there; the first frame,
+    which sees only itself causally, must not."""
+    g = np.random.default_rng(seed)
+    q, k, v = (g.standard_normal((B, T, S, H, d)) for _ in range(3))
+    got = bidir_impl(q, k, v, 0.3)
+    causal = causal_impl(q, k, v, np.zeros((B, 1, S, H, d)), np.zeros((B, 1, S, H, d)), [], 0.3)
+    last = float(np.max(np.abs(got[:, -1] - causal[:, -1])))
+    first_differs = float(np.max(np.abs(got[:, 0] - causal[:, 0]))) > 1e-3
+    return last if first_differs else float("inf")

@@ -4,7 +4,7 @@ import pytest
 
 import synth
 from oracle import (temporal_attn_ref, spatial_attn_ref, spatial_attn_selfrepeat_ref,
-                    softmax_rows)
+                    softmax_rows, bidirectional_temporal_ref, masked_causal_attn_ref)
 import pins
 
 TINY = synth.WORKLOADS["tiny_fp32"]
@@ -85,3 +85,31 @@ def test_softmax_v_all_ones_gives_ones():
     out = temporal_attn_ref(q, k, np.ones((B, n, S, H, d)), rk, np.ones((B, P, S, H, d)),
                             [3, 4, 5, 6, 7, 8, 0, 1, 2], 0.25)
     assert np.max(np.abs(out - 1)) <= 1e-14
+
+
+def test_bidirectional_matches_sdpa():
+    assert pins.check_bidirectional_vs_sdpa(bidirectional_temporal_ref) <= 1e-13
+
+
+def test_bidirectional_zero_keys_mean():
+    assert pins.check_bidirectional_zero_keys(bidirectional_temporal_ref) <= 1e-15
+
+
+def test_bidirectional_permutation():
+    assert pins.check_bidirectional_permutation(bidirectional_temporal_ref) <= 1e-13
+
+
+def test_bidirectional_last_frame_is_causal():
+    assert pins.check_bidirectional_last_frame_is_causal(bidirectional_temporal_ref, temporal_attn_ref) <= 1e-13
+
+
+def test_bidirectional_brute_force_mask():
+    # the explicit-mask form with an all-zero mask, row by row
+    g = np.random.default_rng(15)
+    B, T, S, H, d = 1, 5, 2, 2, 6
+    q, k, v = (g.standard_normal((B, T, S, H, d)) for _ in range(3))
+    got = bidirectional_temporal_ref(q, k, v, 0.4)
+    for s in range(S):
+        for h in range(H):
+            ref = masked_causal_attn_ref(q[0, :, s, h], k[0, :, s, h], v[0, :, s, h], np.zeros((T, T)), 0.4)
+            assert np.max(np.abs(got[0, :, s, h] - ref)) <= 1e-13

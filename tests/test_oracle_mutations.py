@@ -111,3 +111,46 @@ def test_spatial_oracle_passes():
     from oracle import spatial_attn_ref
     assert pins.check_spatial_vs_sdpa(_spatial()) <= 1e-13
     assert pins.check_spatial_vs_sdpa(spatial_attn_ref) <= 1e-13
+
+
+def _bidir(mask_causal=False, use_scale=True, swap_qk=False, axis_bug=False):
+    def impl(q, k, v, scale):
+        q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+        sc = scale if use_scale else 1.0
+        a, b = (k, q) if swap_qk else (q, k)
+        z = sc * np.einsum("btshd,bjshd->bshtj", a, b)
+        T = q.shape[1]
+        if mask_causal:
+            z = z + np.triu(np.full((T, T), -np.inf), 1)
+        if axis_bug:
+            p = np.exp(z - z.max(axis=-2, keepdims=True))
+            p = p / p.sum(axis=-2, keepdims=True)
+        else:
+            p = softmax_rows(z)
+        return np.einsum("bshtj,bjshd->btshd", p, v)
+    return impl
+
+
+def _bidir_pin_fails(impl):
+    from oracle import temporal_attn_ref
+    checks = [
+        lambda: pins.check_bidirectional_vs_sdpa(impl) > 1e-10,
+        lambda: pins.check_bidirectional_zero_keys(impl) > 1e-12,
+        lambda: pins.check_bidirectional_permutation(impl) > 1e-10,
+        lambda: pins.check_bidirectional_last_frame_is_causal(impl, temporal_attn_ref) > 1e-10,
+    ]
+    return any(c() for c in checks)
+
+
+def test_bidirectional_oracle_passes_every_pin():
+    assert not _bidir_pin_fails(_bidir())
+
+
+@pytest.mark.parametrize("mutant", [
+    _bidir(mask_causal=True),      # causal mask where none belongs
+    _bidir(use_scale=False),       # dropped scale
+    _bidir(swap_qk=True),          # Q and K swapped (transposed logits)
+    _bidir(axis_bug=True),         # softmax over the query axis
+], ids=["causal_mask", "no_scale", "swap_qk", "softmax_axis"])
+def test_bidirectional_mutants_fail_a_pin(mutant):
+    assert _bidir_pin_fails(mutant)
