@@ -14,9 +14,12 @@ whole step (the cache-writing pass is timed but its tokens are not counted).
 Also reported: per-kernel average duration from HIP events on the launch
 stream, the dominant kernel's roofline fraction, the batched 32x32-latent
 case (B=8, 1024 tokens) whose temporal working set (1.5 GB) exceeds the
-256 MB Infinity Cache, and the CPU oracle timed on a bounded sample.
+256 MB Infinity Cache, the 80-frame rollout through the cached path against
+the recompute baseline (bidirectional temporal + spatial self attention over
+all conditional frames at every call), and the CPU oracle timed on a bounded
+sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-large]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-large] [--no-rollout]
        python bench.py --kernel {spatial_prefix,temporal,spatial_self,cache_write,qkv_proj}
                        --workload {ar_step_s256,large_b8_s1024,write_b4} --reps R   (one kernel, for profilers)
 """
@@ -42,6 +45,9 @@ N_CACHES = 8      # per-layer caches rotated through at the 256-token shape
 AR_STEP = dict(name="ar_step_s256", B=1, H=16, d=72, S=256, l=8, p_max=25, p_spatial=3, tpe_len=33)
 LARGE = dict(name="large_b8_s1024", B=8, H=16, d=72, S=1024, l=8, p_max=25, p_spatial=3, tpe_len=33)
 WRITE = dict(name="write_b4", B=4, H=16, d=72, S=256, l=8, p_max=41, p_spatial=3, tpe_len=49)
+ROLLOUT = dict(name="rollout_80f", B=1, H=16, d=72, S=256, l=8, p_max=41, p_spatial=3, tpe_len=49)
+ROLLOUT_FRAMES = 80
+ROLLOUT_LAYERS = 8   # attention layers per model call in the rollout comparison
 WORKLOADS = {w["name"]: w for w in (AR_STEP, LARGE, WRITE)}
 KERNELS = ("spatial_prefix", "temporal", "spatial_self", "cache_write", "qkv_proj")
 
@@ -284,6 +290,117 @@ def write_case(reps):
             "bytes_resident": {"shared_cache": shared, "per_timestep_copies_T50": 50 * shared}}
 
 
+def recompute_bytes(sh, T, eb=2):
+    C = sh["H"] * sh["d"]
+    return 4 * T * sh["B"] * sh["S"] * C * eb              # Q, K, V read once, O written
+
+
+def recompute_temporal_flops(sh, T):
+    return sh["B"] * sh["S"] * sh["H"] * T * T * 4 * sh["d"]
+
+
+def rollout_compare():
+    """80-frame rollout (B=1, 256 tokens, 16 heads x 72, chunk 8, P_max 41,
+    P' 3, bf16) through the attention layers of an 8-layer model: the cached
+    path (each AR step: 50 denoising calls of prefix spatial + causal temporal
+    attention over the shared cache, then every layer's cache-writing pass)
+    against the recompute baseline (each AR step: 50 calls of spatial self
+    attention and bidirectional temporal attention over all P_k + 8 frames,
+    no cache). GPU time per AR step from HIP events on the launch stream."""
+    import torch
+    from causal_kv_cache_amd import ca2
+    sh, L = ROLLOUT, ROLLOUT_LAYERS
+    B, l, S, H, d = sh["B"], sh["l"], sh["S"], sh["H"], sh["d"]
+    bf = torch.bfloat16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    chunk = (B, l, S, H, d)
+    t_max = sh["p_max"] + l
+    caches = [ca2.Cache(B, H, d, S, l, sh["p_max"], sh["p_spatial"], sh["tpe_len"], "bf16") for _ in range(L)]
+    first = [_randn((B, 1, S, H, d), gen, bf) for _ in range(4)]
+    for c in caches:
+        c.ca2_cache_write(*first)                    # the conditioning frame
+    sets = [tuple(_randn(chunk, gen, bf) for _ in range(3)) for _ in range(L)]
+    qc, kt, vt, ks, vs = (_randn(chunk, gen, bf) for _ in range(5))
+    full = [tuple(_randn((B, t_max, S, H, d), gen, bf) for _ in range(3)) for _ in range(L)]
+    out_t, out_s = torch.empty(chunk, dtype=bf, device="cuda"), torch.empty(chunk, dtype=bf, device="cuda")
+    full_t = torch.empty((B, t_max, S, H, d), dtype=bf, device="cuda")
+    full_s = torch.empty((B, t_max, S, H, d), dtype=bf, device="cuda")
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def denoise_cached():
+        for _ in range(T_DENOISE):
+            for li in range(L):
+                q, k, v = sets[li]
+                caches[li].ca2_spatial_attn(q, k, v, out_s)
+                caches[li].ca2_temporal_attn(q, k, v, out_t)
+
+    def write_all():
+        for c in caches:
+            c.ca2_temporal_attn(qc, kt, vt, out_t)
+            c.ca2_spatial_attn(qc, ks, vs, out_s, mode=ca2.CA2_SPATIAL_SELF)
+            c.ca2_cache_write(kt, vt, ks, vs)
+
+    steps = []
+    frames = 1
+    while frames < ROLLOUT_FRAMES:
+        p_k = caches[0].ca2_cache_info_get()["p_k"]
+        T = p_k + l
+
+        def recompute():
+            for _ in range(T_DENOISE):
+                for li in range(L):
+                    q, k, v = (x[:, :T] for x in full[li])
+                    ca2.ca2_temporal_attn_frames(q, k, v, full_t[:, :T], causal=False)
+                    ca2.ca2_spatial_attn_frames(q, k, v, full_s[:, :T])
+
+        denoise_cached()                              # warm (reads the cache only)
+        ms_den = timed(denoise_cached)
+        ms_wr = timed(write_all)                      # advances every cache by one chunk
+        recompute()
+        ms_re = timed(recompute)
+        # per denoising call and layer: only the cached path's temporal FLOPs grow with P_k
+        flops = {"cached_spatial": spatial_flops(sh, l, sh["p_spatial"]),
+                 "cached_temporal": temporal_flops(sh, l, p_k),
+                 "recompute_spatial": spatial_flops(sh, T, 0),
+                 "recompute_temporal": recompute_temporal_flops(sh, T)}
+        steps.append(dict(p_k=p_k, frames_attended=T, cached_ms=round(ms_den + ms_wr, 3),
+                          cached_write_pass_ms=round(ms_wr, 3), recompute_ms=round(ms_re, 3),
+                          flops_per_call_layer=flops))
+        frames += l
+    cum_c = cum_r = 0.0
+    for st in steps:
+        cum_c += st["cached_ms"]
+        cum_r += st["recompute_ms"]
+        st["cumulative_cached_ms"] = round(cum_c, 3)
+        st["cumulative_recompute_ms"] = round(cum_r, 3)
+    # the recompute kernels at the largest step, on their own rooflines
+    T = t_max
+    q, k, v = full[0]
+    us_t = time_launches(lambda: ca2.ca2_temporal_attn_frames(q, k, v, full_t, causal=False), 50)
+    us_s = time_launches(lambda: ca2.ca2_spatial_attn_frames(q, k, v, full_s), 20)
+    by, fl_t, fl_s = recompute_bytes(sh, T), recompute_temporal_flops(sh, T), spatial_flops(sh, T, 0)
+    for c in caches:
+        c.close()
+    return {"workload": sh["name"], "layers": L, "denoise_calls_per_step": T_DENOISE,
+            "steps": steps, "total_speedup": round(cum_r / cum_c, 3),
+            "recompute_kernels_at_T%d" % T: {
+                "temporal_bidirectional": {"us": round(us_t, 3), "bytes": by, "flops": fl_t,
+                                           "achieved_gbs": round(by / us_t / 1e3, 1),
+                                           "frac_hbm": round(by / us_t / 1e3 / HBM_PEAK_GBS, 4)},
+                "spatial_self_frames": {"us": round(us_s, 3), "flops": fl_s,
+                                        "achieved_tflops": round(fl_s / us_s / 1e6, 1),
+                                        "frac_mfma": round(fl_s / us_s / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)}}}
+
+
 def kernel_mode(kernel, workload, reps):
     """Launch one kernel of one workload `reps` times (for profilers)."""
     import torch
@@ -344,6 +461,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-large", action="store_true")
+    ap.add_argument("--no-rollout", action="store_true")
     ap.add_argument("--kernel", choices=KERNELS, help="only launch this kernel (profiling mode)")
     ap.add_argument("--workload", choices=tuple(WORKLOADS), default=AR_STEP["name"])
     ap.add_argument("--reps", type=int, default=20)
@@ -420,6 +538,9 @@ def main():
         del wl
         torch.cuda.empty_cache()
         result["write_case"] = write_case(max(10, args.kernel_reps // 10))
+        torch.cuda.empty_cache()
+    if not args.no_rollout:
+        result["rollout_cached_vs_recompute"] = rollout_compare()
         torch.cuda.empty_cache()
 
     if not args.no_cpu:

@@ -62,6 +62,10 @@ _SIGS = {
     "ca2_bytes_resident": (ctypes.c_uint64, [ctypes.POINTER(Ca2Config)]),
     "ca2_cache_debug_copy": (_I32, [_P, _P, _P, _P, _P, _P]),
     "ca2_qkv_proj": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
+    "ca2_temporal_attn_frames": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                        ctypes.c_float, _P]),
+    "ca2_spatial_attn_frames": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                       ctypes.c_float, _P]),
     "ca2_status_string": (ctypes.c_char_p, [_I32]),
     "ca2_last_error": (ctypes.c_char_p, []),
 }
@@ -179,6 +183,40 @@ def ca2_qkv_proj(x, w, q, k, v, stream=None):
             raise ValueError(f"qkv_proj: expected contiguous cuda bf16 {shape}, got {t.dtype} {tuple(t.shape)}")
     _check(load().ca2_qkv_proj(_ptr(x), _ptr(w), _ptr(q), _ptr(k), _ptr(v), m, c_in, c,
                                _stream(stream)), "ca2_qkv_proj")
+
+
+def _frames_shape(q, k, v, out, where):
+    """[B][T][S][H][d] cuda tensors of one dtype -> (B, T, S, H, d, ca2 dtype)."""
+    import torch
+    dt = {torch.float32: CA2_F32, torch.bfloat16: CA2_BF16}.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"{where}: dtype {q.dtype} is not float32 or bfloat16")
+    if q.dim() != 5:
+        raise ValueError(f"{where}: expected [B][T][S][H][d] tensors, got {tuple(q.shape)}")
+    for t in (q, k, v, out):
+        if t.dtype != q.dtype or tuple(t.shape) != tuple(q.shape) or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{where}: expected contiguous cuda {q.dtype} {tuple(q.shape)}, "
+                             f"got {t.dtype} {tuple(t.shape)}")
+    B, T, S, H, d = q.shape
+    return B, T, S, H, d, dt
+
+
+def ca2_temporal_attn_frames(q, k, v, out, causal, scale=None, stream=None):
+    """Cache-less temporal attention over the T frames of [B][T][S][H][d]
+    tensors: causal (mask over frames) or bidirectional (causal=False)."""
+    B, T, S, H, d, dt = _frames_shape(q, k, v, out, "ca2_temporal_attn_frames")
+    sc = d ** -0.5 if scale is None else scale
+    _check(load().ca2_temporal_attn_frames(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, S, H, d, dt,
+                                           1 if causal else 0, sc, _stream(stream)),
+           "ca2_temporal_attn_frames")
+
+
+def ca2_spatial_attn_frames(q, k, v, out, scale=None, stream=None):
+    """Cache-less spatial self attention of each of the T frames."""
+    B, T, S, H, d, dt = _frames_shape(q, k, v, out, "ca2_spatial_attn_frames")
+    sc = d ** -0.5 if scale is None else scale
+    _check(load().ca2_spatial_attn_frames(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, S, H, d, dt, sc,
+                                          _stream(stream)), "ca2_spatial_attn_frames")
 
 
 class Cache:

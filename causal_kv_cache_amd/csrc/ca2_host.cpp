@@ -92,6 +92,21 @@ ca2_status check_ptrs(std::initializer_list<const void*> ps) {
   return CA2_OK;
 }
 
+// Shape checks of the cache-less entry points ([B][T][S][H][d] tensors).
+ca2_status check_frames_shape(int32_t B, int32_t T, int32_t S, int32_t H, int32_t d, int32_t dtype,
+                              float scale) {
+  if (dtype != CA2_F32 && dtype != CA2_BF16) return fail(CA2_ERR_INVALID_ARG, "dtype %d", dtype);
+  if (B < 1 || T < 1 || S < 1 || H < 1 || d < 1)
+    return fail(CA2_ERR_INVALID_ARG, "batch/frames/tokens/heads/head_dim must be >= 1");
+  if (T > 4096) return fail(CA2_ERR_INVALID_ARG, "frames %d > 4096", T);
+  if ((int64_t)T * H > 65535) return fail(CA2_ERR_INVALID_ARG, "frames * heads > 65535");
+  if ((int64_t)B * S * H > ((int64_t)1 << 30)) return fail(CA2_ERR_INVALID_ARG, "B*S*H too large");
+  if ((int64_t)B * T * S * H * d * elem_bytes(dtype) > ((int64_t)1 << 46))
+    return fail(CA2_ERR_INVALID_ARG, "tensor too large");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(CA2_ERR_INVALID_ARG, "scale must be finite and > 0");
+  return CA2_OK;
+}
+
 ca2_status hip_fail(hipError_t e, const char* what) {
   return fail(CA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -249,6 +264,7 @@ ca2_status ca2_temporal_attn(const ca2_cache* c, const void* q, const void* k_ne
   a.p_k = queue_len(c);
   a.head = queue_head(c);
   a.p_max = c->cfg.p_max;
+  a.causal = 1;
   a.scale_log2e = scale * 1.4426950408889634f;
   hipError_t e = ca2::launch_temporal(c->cfg.dtype, c->cfg.head_dim, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "temporal_attn launch");
@@ -280,6 +296,54 @@ ca2_status ca2_spatial_attn(const ca2_cache* c, const void* q, const void* k, co
   a.scale_log2e = scale * 1.4426950408889634f;
   hipError_t e = ca2::launch_spatial(c->cfg.dtype, c->cfg.head_dim, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "spatial_attn launch");
+  return ok();
+}
+
+ca2_status ca2_temporal_attn_frames(const void* q, const void* k, const void* v, void* out, int32_t B,
+                                    int32_t T, int32_t S, int32_t H, int32_t d, int32_t dtype, int32_t causal,
+                                    float scale, void* stream) {
+  ca2_status st = check_frames_shape(B, T, S, H, d, dtype, scale);
+  if (st != CA2_OK) return st;
+  st = check_ptrs({q, k, v, out});
+  if (st != CA2_OK) return st;
+  if (causal != 0 && causal != 1) return fail(CA2_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!ca2::temporal_supported(dtype, d))
+    return fail(CA2_ERR_UNSUPPORTED, "head_dim %d not built for dtype %d", d, dtype);
+  ca2::TemporalArgs a;
+  a.q = q; a.k_new = k; a.v_new = v; a.out = out;
+  a.ring_k = k; a.ring_v = v;   // never read: the queue is empty
+  a.rows_per_batch = S * H;
+  a.rows_total = B * a.rows_per_batch;
+  a.n = T;
+  a.p_k = 0;
+  a.head = 0;
+  a.p_max = 1;
+  a.causal = causal;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  hipError_t e = ca2::launch_temporal(dtype, d, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "temporal_attn_frames launch");
+  return ok();
+}
+
+ca2_status ca2_spatial_attn_frames(const void* q, const void* k, const void* v, void* out, int32_t B,
+                                   int32_t T, int32_t S, int32_t H, int32_t d, int32_t dtype, float scale,
+                                   void* stream) {
+  ca2_status st = check_frames_shape(B, T, S, H, d, dtype, scale);
+  if (st != CA2_OK) return st;
+  st = check_ptrs({q, k, v, out});
+  if (st != CA2_OK) return st;
+  if (!ca2::spatial_supported(dtype, d))
+    return fail(CA2_ERR_UNSUPPORTED, "head_dim %d not built for dtype %d", d, dtype);
+  ca2::SpatialArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.sp_k = nullptr; a.sp_v = nullptr;
+  a.batch = B; a.n = T; a.tokens = S; a.heads = H;
+  a.p_slots = 0;
+  a.n_prefix = 0;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  hipError_t e = ca2::launch_spatial(dtype, d, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "spatial_attn_frames launch");
   return ok();
 }
 

@@ -7,7 +7,10 @@
 
 namespace ca2 {
 
-// Causal temporal attention over the queue + new frames (one launch).
+// Temporal attention over the queue + new frames (one launch). With
+// causal = 1, new frame i sees the queue and new frames 0..i; with causal = 0
+// every new frame sees every key (the cache-less recompute form, p_k = 0).
+// The launch covers any n >= 1: query frames are cut into blocks along grid y.
 struct TemporalArgs {
   const void* q;
   const void* k_new;
@@ -21,6 +24,7 @@ struct TemporalArgs {
   int32_t p_k;             // queued frames
   int32_t head;            // ring slot of the oldest queued frame
   int32_t p_max;           // ring slots
+  int32_t causal;          // 1: lower-triangular mask over the new frames; 0: no mask
   float scale_log2e;       // softmax scale * log2(e)
 };
 

@@ -3,7 +3,10 @@
 // Computes, for every row (b, s, h) and new frame i < n, softmax over the
 // P_k queued frames plus new frames 0..i of scale * q_i . k, times V
 // (Ca2-VDM notes, key design 1: CausalAttn equation with a lower-triangular
-// mask; key design 4: the queue of at most P_max cached frames).
+// mask; key design 4: the queue of at most P_max cached frames). With the
+// mask switched off and an empty queue the same kernels compute the
+// bidirectional temporal attention of the recompute baseline (abstract page:
+// problem statement; notes: speed comparison with OS-Ext).
 //
 // Work mapping (HBM-bound: each K/V byte is used by at most n queries):
 //   * a wavefront owns ROWS = 64/QL consecutive rows; lane = (row, query),
@@ -57,7 +60,8 @@ __global__ __launch_bounds__(64 * kWaves) void temporal_attn_kernel(TemporalArgs
   const int wave = threadIdx.x >> 6;
   const int row0 = blockIdx.x * ROWS;
   const int ri = lane / QL;
-  const int qi = lane % QL;
+  const int q0 = blockIdx.y * QL;           // first query frame of this block
+  const int qi = q0 + lane % QL;
   const int row = row0 + ri;
   const bool active = row < a.rows_total && qi < a.n;
   const int rpb = a.rows_per_batch;
@@ -102,8 +106,10 @@ __global__ __launch_bounds__(64 * kWaves) void temporal_attn_kernel(TemporalArgs
 
   uint4* stage = lds + wave * C::STAGE_U4;
   const int k_total = a.p_k + a.n;
-  const int n_blocks = (k_total + F - 1) / F;
-  const int last_key = a.p_k + qi;          // keys 0..last_key are visible
+  // keys any query of the block can see
+  const int k_lim = a.causal ? min(k_total, a.p_k + q0 + QL) : k_total;
+  const int n_blocks = (k_lim + F - 1) / F;
+  const int last_key = a.causal ? a.p_k + qi : k_total - 1;   // keys 0..last_key are visible
   const int64_t frame_elems = (int64_t)rpb * D;
 
   float m = -INFINITY, l = 0.f;
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(64 * kWaves) void temporal_attn_kernel(TemporalArgs
       const int j = j0 + ch_fo[c];
       kr[c] = make_uint4(0, 0, 0, 0);
       vr[c] = make_uint4(0, 0, 0, 0);
-      if (ch_ok[c] && j < k_total) {
+      if (ch_ok[c] && j < k_lim) {
         const T* kb;
         const T* vb;
         int64_t base;
@@ -166,7 +172,7 @@ __global__ __launch_bounds__(64 * kWaves) void temporal_attn_kernel(TemporalArgs
         for (int e = 0; e < VPC; ++e) s = fmaf(qf[c * VPC + e], kv[e], s);
       }
       const int j = j0 + fo;
-      const bool vis = active && j <= last_key && j < k_total;
+      const bool vis = active && j <= last_key && j < k_lim;
       sc[fo] = vis ? s * a.scale_log2e : -INFINITY;
       mb = fmaxf(mb, sc[fo]);
     }
@@ -329,6 +335,7 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
   const int g = lane & 3;                          // dimension group
   const int qg = (lane >> 2) % QH;                 // query group
   const int ri = lane / LPR;
+  const int q0 = blockIdx.y * (kQPL * QH);         // first query frame of this block
   const int row = blockIdx.x * ROWS + ri;
   const bool row_ok = row < a.rows_total;
   const int rpb = a.rows_per_batch;
@@ -343,15 +350,16 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
   const unsigned char* rkb = static_cast<const unsigned char*>(a.ring_k);
   const unsigned char* rvb = static_cast<const unsigned char*>(a.ring_v);
 
-  // queries of this lane: frames qg*4 .. qg*4+3 (dims of this lane only)
+  // queries of this lane: frames q0+qg*4 .. q0+qg*4+3 (dims of this lane only)
+  const int k_total = a.p_k + a.n;
   Slice<D> qs[kQPL];
   bool qok[kQPL];
   int last_key[kQPL];
 #pragma unroll
   for (int qq = 0; qq < kQPL; ++qq) {
-    const int qi = qg * kQPL + qq;
+    const int qi = q0 + qg * kQPL + qq;
     qok[qq] = row_ok && qi < a.n;
-    last_key[qq] = qok[qq] ? a.p_k + qi : -1;
+    last_key[qq] = !qok[qq] ? -1 : a.causal ? a.p_k + qi : k_total - 1;
     if (qok[qq]) {
       load_slice<D>(qs[qq], qb + ((int64_t)b * a.n + qi) * frame_bytes + row_bytes, g);
     } else {
@@ -360,11 +368,11 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
     }
   }
 
-  // key range of this wavefront
-  const int k_total = a.p_k + a.n;
-  const int per = (k_total + splits - 1) / splits;
+  // key range of this wavefront, within the keys the block's queries can see
+  const int k_lim = a.causal ? min(k_total, a.p_k + q0 + kQPL * QH) : k_total;
+  const int per = (k_lim + splits - 1) / splits;
   const int kb = wave * per;
-  const int ke = min(k_total, kb + per);
+  const int ke = min(k_lim, kb + per);
 
   auto key_row = [&](int j, const unsigned char* ring, const unsigned char* fresh) -> const unsigned char* {
     if (j < a.p_k) {
@@ -484,7 +492,7 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
 #pragma unroll
   for (int qq = 0; qq < kQPL; ++qq) {
     if (!qok[qq]) continue;
-    const int qi = qg * kQPL + qq;
+    const int qi = q0 + qg * kQPL + qq;
     const float inv = 1.f / l[qq];
     float o[DPL];
 #pragma unroll
@@ -496,14 +504,18 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
 template <int D, int QH>
 hipError_t launch_ds_q(const TemporalArgs& a, hipStream_t s) {
   constexpr int ROWS = 64 / (4 * QH);
+  constexpr int QB = kQPL * QH;                    // query frames per block
   const int groups = (a.rows_total + ROWS - 1) / ROWS;
-  // split the key range when there are too few row groups to fill the chip
-  int splits = (2048 + groups - 1) / groups;
+  const int qblocks = (a.n + QB - 1) / QB;
+  if (qblocks > 65535) return hipErrorInvalidValue;
+  // split the key range when there are too few workgroups to fill the chip
+  const int64_t wgs = (int64_t)groups * qblocks;
+  int splits = (int)((2048 + wgs - 1) / wgs);
   splits = splits < 1 ? 1 : splits > 4 ? 4 : splits;
-  const int k_total = a.p_k + a.n;
-  if (splits > k_total) splits = k_total;
+  const int k_min = a.causal ? a.p_k + (a.n < QB ? a.n : QB) : a.p_k + a.n;   // fewest keys of a block
+  if (splits > k_min) splits = k_min;
   const size_t lds = splits > 1 ? (size_t)(splits - 1) * 64 * kQPL * (DsGeom<D>::DPL + 2) * sizeof(float) : 0;
-  hipLaunchKernelGGL((temporal_attn_ds_kernel<D, QH>), dim3(groups), dim3(64 * splits), lds, s, a, splits);
+  hipLaunchKernelGGL((temporal_attn_ds_kernel<D, QH>), dim3(groups, qblocks), dim3(64 * splits), lds, s, a, splits);
   return hipGetLastError();
 }
 
@@ -518,7 +530,9 @@ template <typename T, int D>
 hipError_t launch_td(const TemporalArgs& a, hipStream_t s) {
   const int ql = a.n <= 4 ? 4 : a.n <= 8 ? 8 : 16;
   const int rows = 64 / ql;
-  const dim3 grid((a.rows_total + rows - 1) / rows);
+  const int qblocks = (a.n + ql - 1) / ql;
+  if (qblocks > 65535) return hipErrorInvalidValue;
+  const dim3 grid((a.rows_total + rows - 1) / rows, qblocks);
   const dim3 block(64 * kWaves);
   if (ql == 4) hipLaunchKernelGGL((temporal_attn_kernel<T, D, 4>), grid, block, 0, s, a);
   else if (ql == 8) hipLaunchKernelGGL((temporal_attn_kernel<T, D, 8>), grid, block, 0, s, a);
@@ -535,7 +549,7 @@ bool temporal_supported(int dtype, int d) {
 }
 
 hipError_t launch_temporal(int dtype, int d, const TemporalArgs& a, hipStream_t s) {
-  if (a.n < 1 || a.n > 16) return hipErrorInvalidValue;
+  if (a.n < 1 || a.p_k < 0) return hipErrorInvalidValue;
   if (dtype == 0) {
     switch (d) {
       case 16: return launch_td<float, 16>(a, s);

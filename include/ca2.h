@@ -145,6 +145,33 @@ ca2_status ca2_spatial_attn(const ca2_cache* cache, const void* q, const void* k
                             float scale, void* stream);
 
 /*
+ * Cache-less temporal attention over T frames, [B][T][S][H][d] tensors in
+ * `dtype` (ca2_dtype): for each row (b, s, h) and frame t, out_t =
+ * softmax(scale * q_t . K^T) V over keys 0..t (causal = 1: full causal
+ * attention over the concatenated sequence, which the cached path must
+ * reproduce -- [notes] key design 1) or over all T keys (causal = 0: the
+ * bidirectional temporal attention of the recompute baseline, which must see
+ * every conditional frame again at every step -- [abstract] problem
+ * statement; [notes] speed comparison with OS-Ext). 1 <= T <= 4096,
+ * T * heads <= 65535; head_dim as for the cache. Touches no cache.
+ */
+ca2_status ca2_temporal_attn_frames(const void* q, const void* k, const void* v, void* out,
+                                    int32_t batch, int32_t frames, int32_t tokens, int32_t heads,
+                                    int32_t head_dim, int32_t dtype, int32_t causal, float scale,
+                                    void* stream);
+
+/*
+ * Cache-less spatial self attention of each of T frames (keys/values are the
+ * frame's own S tokens): the spatial layer of the recompute baseline, which
+ * recomputes every conditional frame's spatial attention at every step
+ * ([notes] FLOPs comparison of the attention layers under extended
+ * conditioning). Same tensors and limits as ca2_temporal_attn_frames.
+ */
+ca2_status ca2_spatial_attn_frames(const void* q, const void* k, const void* v, void* out,
+                                   int32_t batch, int32_t frames, int32_t tokens, int32_t heads,
+                                   int32_t head_dim, int32_t dtype, float scale, void* stream);
+
+/*
  * Cyclic TPE indices of the next n frames ([notes] key design 4,
  * Cyclic-TPEs): host_out[i] = (frames_written + i) mod tpe_len, frame 0 being
  * the conditioning frame. Host-only; host_out has n_frames entries.

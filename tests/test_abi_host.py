@@ -114,3 +114,24 @@ def test_null_and_range_errors(lib):
         assert lib.ca2_status_string(s)
     assert raw.ca2_tpe_index_raw(-1, 2, 13, None) == lib.CA2_ERR_INVALID_ARG
     assert raw.ca2_last_error().decode()        # the failing call left a detail string
+
+
+def test_frames_entry_points_reject_bad_arguments(lib):
+    # every case fails validation before anything is launched
+    raw = lib.load()
+    p = ctypes.c_void_p(4096)          # aligned, never dereferenced
+    t, s = raw.ca2_temporal_attn_frames, raw.ca2_spatial_attn_frames
+    BAD, UNS = lib.CA2_ERR_INVALID_ARG, lib.CA2_ERR_UNSUPPORTED
+    assert t(None, p, p, p, 1, 4, 16, 2, 64, 1, 0, 0.125, None) == BAD        # NULL q
+    assert t(p, p, p, ctypes.c_void_p(4100), 1, 4, 16, 2, 64, 1, 0, 0.125, None) == BAD   # misaligned
+    assert t(p, p, p, p, 1, 0, 16, 2, 64, 1, 0, 0.125, None) == BAD           # T = 0
+    assert t(p, p, p, p, 1, 4097, 16, 2, 64, 1, 0, 0.125, None) == BAD        # T > 4096
+    assert t(p, p, p, p, 1, 4096, 16, 16, 64, 1, 0, 0.125, None) == BAD       # T * H > 65535
+    assert t(p, p, p, p, 1, 4, 16, 2, 64, 1, 2, 0.125, None) == BAD           # causal not 0/1
+    assert t(p, p, p, p, 1, 4, 16, 2, 64, 1, 0, 0.0, None) == BAD             # scale 0
+    assert t(p, p, p, p, 1, 4, 16, 2, 64, 7, 0, 0.125, None) == BAD           # dtype
+    assert t(p, p, p, p, 1, 4, 16, 2, 16, 1, 0, 0.125, None) == UNS           # bf16 d=16 not built
+    assert s(p, p, p, p, 1, 4, 16, 2, 16, 1, 0.125, None) == UNS
+    assert s(p, p, p, p, 1, 4, 16, 2, 64, 1, float("nan"), None) == BAD
+    assert s(p, p, p, None, 1, 4, 16, 2, 64, 1, 0.125, None) == BAD
+    assert "NULL" in raw.ca2_last_error().decode()
