@@ -372,8 +372,18 @@ def rollout_compare():
                  "cached_temporal": temporal_flops(sh, l, p_k),
                  "recompute_spatial": spatial_flops(sh, T, 0),
                  "recompute_temporal": recompute_temporal_flops(sh, T)}
+        # the same work at the spec rooflines (each kernel at max(bytes/HBM, flops/MFMA))
+        def ideal_us(by, fl):
+            return max(by / HBM_PEAK_GBS / 1e3, fl / MFMA_BF16_PEAK_TFLOPS / 1e6)
+        calls = T_DENOISE * L
+        ideal_c = calls * (ideal_us(spatial_bytes(sh, l, sh["p_spatial"]), flops["cached_spatial"]) +
+                           ideal_us(temporal_bytes(sh, l, p_k), flops["cached_temporal"]))
+        ideal_r = calls * (ideal_us(spatial_bytes(sh, T, 0), flops["recompute_spatial"]) +
+                           ideal_us(recompute_bytes(sh, T), flops["recompute_temporal"]))
         steps.append(dict(p_k=p_k, frames_attended=T, cached_ms=round(ms_den + ms_wr, 3),
                           cached_write_pass_ms=round(ms_wr, 3), recompute_ms=round(ms_re, 3),
+                          ideal_cached_denoise_ms=round(ideal_c / 1e3, 3),
+                          ideal_recompute_ms=round(ideal_r / 1e3, 3),
                           flops_per_call_layer=flops))
         frames += l
     cum_c = cum_r = 0.0
@@ -390,8 +400,11 @@ def rollout_compare():
     by, fl_t, fl_s = recompute_bytes(sh, T), recompute_temporal_flops(sh, T), spatial_flops(sh, T, 0)
     for c in caches:
         c.close()
+    ideal_c = sum(st["ideal_cached_denoise_ms"] for st in steps)
+    ideal_r = sum(st["ideal_recompute_ms"] for st in steps)
     return {"workload": sh["name"], "layers": L, "denoise_calls_per_step": T_DENOISE,
             "steps": steps, "total_speedup": round(cum_r / cum_c, 3),
+            "total_speedup_at_spec_rooflines": round(ideal_r / ideal_c, 3),
             "recompute_kernels_at_T%d" % T: {
                 "temporal_bidirectional": {"us": round(us_t, 3), "bytes": by, "flops": fl_t,
                                            "achieved_gbs": round(by / us_t / 1e3, 1),
