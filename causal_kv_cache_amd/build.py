@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libca2.so")
 
-SOURCES = ["ca2_host.cpp", "temporal_attn.hip", "spatial_attn.hip", "cache_write.hip", "qkv_proj.hip"]
+SOURCES = ["ca2_host.cpp", "temporal_attn.hip", "spatial_attn.hip", "cache_write.hip", "qkv_proj.hip",
+           "toy_block.hip"]
 ARCH = "gfx950"
 
 

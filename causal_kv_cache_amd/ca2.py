@@ -66,6 +66,9 @@ _SIGS = {
                                         ctypes.c_float, _P]),
     "ca2_spatial_attn_frames": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                        ctypes.c_float, _P]),
+    "ca2_toy_temb_mod": (_I32, [_P, _I32, _P, _I32, _I32, _P, _P]),
+    "ca2_toy_ln_mod": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P]),
+    "ca2_toy_linear": (_I32, [_P, _I32, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _P]),
     "ca2_status_string": (ctypes.c_char_p, [_I32]),
     "ca2_last_error": (ctypes.c_char_p, []),
 }
@@ -217,6 +220,56 @@ def ca2_spatial_attn_frames(q, k, v, out, scale=None, stream=None):
     sc = d ** -0.5 if scale is None else scale
     _check(load().ca2_spatial_attn_frames(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, S, H, d, dt, sc,
                                           _stream(stream)), "ca2_spatial_attn_frames")
+
+
+def _f32_2d(t, where):
+    import torch
+    if t.dtype != torch.float32 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{where}: expected a 2-D cuda float32 tensor with unit column stride, "
+                         f"got {t.dtype} {tuple(t.shape)} strides {t.stride()}")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def ca2_toy_temb_mod(t, wmod, out, stream=None):
+    """t: [F] float32, wmod: [temb_dim][W], out: [F][W] (cuda)."""
+    import torch
+    if t.dtype != torch.float32 or t.dim() != 1 or not t.is_contiguous():
+        raise ValueError("ca2_toy_temb_mod: t must be a contiguous 1-D float32 tensor")
+    td, wd, _ = _f32_2d(wmod, "ca2_toy_temb_mod")
+    f, w2, _ = _f32_2d(out, "ca2_toy_temb_mod")
+    if not (wmod.is_contiguous() and out.is_contiguous()) or f != t.shape[0] or w2 != wd:
+        raise ValueError("ca2_toy_temb_mod: shapes do not match")
+    _check(load().ca2_toy_temb_mod(_ptr(t), f, _ptr(wmod), td, wd, _ptr(out), _stream(stream)), "ca2_toy_temb_mod")
+
+
+def ca2_toy_ln_mod(x, mod, shift_off, scale_off, out, stream=None):
+    """x, out: [F][S][C] float32; mod: [F][W] with the shift and scale ranges inside W."""
+    import torch
+    for u in (x, out, mod):
+        if u.dtype != torch.float32 or not u.is_contiguous() or not u.is_cuda:
+            raise ValueError("ca2_toy_ln_mod: contiguous cuda float32 tensors expected")
+    if x.dim() != 3 or tuple(out.shape) != tuple(x.shape) or mod.dim() != 2 or mod.shape[0] != x.shape[0]:
+        raise ValueError("ca2_toy_ln_mod: shapes do not match")
+    F, S, C = x.shape
+    _check(load().ca2_toy_ln_mod(_ptr(x), _ptr(mod), mod.shape[1], shift_off, scale_off, F, S, C, _ptr(out),
+                                 _stream(stream)), "ca2_toy_ln_mod")
+
+
+def ca2_toy_linear(x, w, y, r=None, act=0, stream=None):
+    """y = act(x @ w) (+ r); 2-D cuda float32 views with unit column stride
+    (column slices of a wider matrix are fine)."""
+    m, k, ldx = _f32_2d(x, "ca2_toy_linear")
+    k2, n, ldw = _f32_2d(w, "ca2_toy_linear")
+    m2, n2, ldy = _f32_2d(y, "ca2_toy_linear")
+    ldr = 0
+    if r is not None:
+        m3, n3, ldr = _f32_2d(r, "ca2_toy_linear")
+        if (m3, n3) != (m, n):
+            raise ValueError("ca2_toy_linear: r shape")
+    if k2 != k or (m2, n2) != (m, n):
+        raise ValueError(f"ca2_toy_linear: shapes {tuple(x.shape)} @ {tuple(w.shape)} -> {tuple(y.shape)}")
+    _check(load().ca2_toy_linear(_ptr(x), ldx, _ptr(w), ldw, _ptr(r), ldr, _ptr(y), ldy, m, n, k, act,
+                                 _stream(stream)), "ca2_toy_linear")
 
 
 class Cache:

@@ -435,4 +435,44 @@ ca2_status ca2_qkv_proj(const void* x, const void* w, void* q, void* k, void* v,
   return ok();
 }
 
+ca2_status ca2_toy_temb_mod(const float* t, int32_t frames, const float* wmod, int32_t temb_dim, int32_t width,
+                            float* out, void* stream) {
+  ca2_status st = check_ptrs({t, wmod, out});
+  if (st != CA2_OK) return st;
+  if (frames < 1 || frames > 65535 || temb_dim < 2 || temb_dim % 2 || width < 1)
+    return fail(CA2_ERR_INVALID_ARG, "frames in [1, 65535], temb_dim even >= 2, width >= 1");
+  hipError_t e = ca2::launch_toy_temb_mod(t, frames, wmod, temb_dim, width, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "toy_temb_mod launch");
+  return ok();
+}
+
+ca2_status ca2_toy_ln_mod(const float* x, const float* mod, int32_t mod_stride, int32_t shift_off,
+                          int32_t scale_off, int32_t frames, int32_t tokens, int32_t channels, float* out,
+                          void* stream) {
+  ca2_status st = check_ptrs({x, mod, out});
+  if (st != CA2_OK) return st;
+  if (frames < 1 || tokens < 1 || channels < 1 || (int64_t)frames * tokens > 0x7fffffff)
+    return fail(CA2_ERR_INVALID_ARG, "frames, tokens, channels >= 1");
+  if (shift_off < 0 || scale_off < 0 || shift_off + channels > mod_stride || scale_off + channels > mod_stride)
+    return fail(CA2_ERR_INVALID_ARG, "shift/scale ranges must lie inside a mod row");
+  hipError_t e = ca2::launch_toy_ln_mod(x, mod, mod_stride, shift_off, scale_off, tokens, frames * tokens, channels,
+                                        out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "toy_ln_mod launch");
+  return ok();
+}
+
+ca2_status ca2_toy_linear(const float* x, int32_t ldx, const float* w, int32_t ldw, const float* r, int32_t ldr,
+                          float* y, int32_t ldy, int32_t m, int32_t n, int32_t k, int32_t act, void* stream) {
+  if (!x || !w || !y) return fail(CA2_ERR_INVALID_ARG, "x, w and y must not be NULL");
+  if (m < 1 || n < 1 || k < 1 || m > (1 << 20) || n > (1 << 20))
+    return fail(CA2_ERR_INVALID_ARG, "m, n, k >= 1 (m, n <= 2^20)");
+  if (ldx < k || ldw < n || ldy < n || (r && ldr < n))
+    return fail(CA2_ERR_INVALID_ARG, "leading dimensions smaller than the rows they hold");
+  if (act != 0 && act != 1) return fail(CA2_ERR_INVALID_ARG, "act must be 0 (identity) or 1 (GELU)");
+  ca2::ToyLinearArgs a{x, w, r, y, m, n, k, ldx, ldw, r ? ldr : 0, ldy, act};
+  hipError_t e = ca2::launch_toy_linear(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "toy_linear launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -69,12 +69,30 @@ struct ProjArgs {
   int32_t m, c_in, c_out;
 };
 
+// fp32 linear layer of the toy block: y = act(x w) (+ r), row-major with
+// leading dimensions in elements; act 0 = identity, 1 = tanh-form GELU.
+struct ToyLinearArgs {
+  const float* x;
+  const float* w;
+  const float* r;   // may be NULL; may alias y
+  float* y;
+  int32_t m, n, k;
+  int32_t ldx, ldw, ldr, ldy;
+  int32_t act;
+};
+
 // Each launcher returns hipSuccess or the launch error; it returns
 // hipErrorInvalidValue for a (dtype, head_dim) pair that is not built.
 hipError_t launch_temporal(int dtype, int head_dim, const TemporalArgs& a, hipStream_t s);
 hipError_t launch_spatial(int dtype, int head_dim, const SpatialArgs& a, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s);
+
+hipError_t launch_toy_temb_mod(const float* t, int frames, const float* wmod, int temb_dim, int width, float* out,
+                               hipStream_t s);
+hipError_t launch_toy_ln_mod(const float* x, const float* mod, int mod_stride, int shift_off, int scale_off,
+                             int tokens, int rows, int C, float* out, hipStream_t s);
+hipError_t launch_toy_linear(const ToyLinearArgs& a, hipStream_t s);
 
 bool temporal_supported(int dtype, int head_dim);
 bool spatial_supported(int dtype, int head_dim);

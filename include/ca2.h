@@ -227,6 +227,36 @@ ca2_status ca2_cache_debug_copy(const ca2_cache* cache, void* host_k, void* host
 ca2_status ca2_qkv_proj(const void* x, const void* w, void* q, void* k, void* v,
                         int32_t m, int32_t c_in, int32_t c_out, void* stream);
 
+/*
+ * Pieces of a small spatial-temporal transformer block (random weights) for
+ * end-to-end checks of the shared cache on the GPU: the block's attention
+ * runs through ca2_spatial_attn / ca2_temporal_attn / ca2_cache_write, these
+ * compute what surrounds it. Clean frames take timestep 0 and targets the
+ * denoising timestep, one entry per frame ([notes] key design 2, cache
+ * sharing with tEmb(0); training section, per-frame timestep vector). All
+ * device buffers are fp32, row-major, owned by the caller.
+ *
+ * ca2_toy_temb_mod: out[f][j] = sum_i emb(t[f])[i] * wmod[i][j] with
+ *   emb(t) = [sin(t w_0), .., sin(t w_{h-1}), cos(t w_0), .., cos(t w_{h-1})],
+ *   h = temb_dim / 2, w_i = 1000^(-i/h) (evaluated in double). t: [frames];
+ *   wmod: [temb_dim][width]; out: [frames][width]. temb_dim even.
+ * ca2_toy_ln_mod: for each token row (f, s) of x [frames][tokens][channels]:
+ *   out = (x - mean) / sqrt(var + 1e-6) * (1 + mod[f][scale_off + c])
+ *         + mod[f][shift_off + c]; mod rows have mod_stride floats.
+ * ca2_toy_linear: y[i][j] = act(sum_k x[i][k] w[k][j]) + (r ? r[i][j] : 0),
+ *   x [m][k] (ldx), w [k][n] (ldw), r and y [m][n] (ldr, ldy; y may equal r);
+ *   act 0 = identity, 1 = GELU, tanh form. Pointers need 4-byte alignment.
+ * Errors: INVALID_ARG for NULL or out-of-range sizes, HIP for launch failures.
+ */
+ca2_status ca2_toy_temb_mod(const float* t, int32_t frames, const float* wmod, int32_t temb_dim,
+                            int32_t width, float* out, void* stream);
+ca2_status ca2_toy_ln_mod(const float* x, const float* mod, int32_t mod_stride, int32_t shift_off,
+                          int32_t scale_off, int32_t frames, int32_t tokens, int32_t channels,
+                          float* out, void* stream);
+ca2_status ca2_toy_linear(const float* x, int32_t ldx, const float* w, int32_t ldw, const float* r,
+                          int32_t ldr, float* y, int32_t ldy, int32_t m, int32_t n, int32_t k,
+                          int32_t act, void* stream);
+
 /* Static description of a status code. */
 const char* ca2_status_string(ca2_status status);
 

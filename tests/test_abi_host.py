@@ -135,3 +135,17 @@ def test_frames_entry_points_reject_bad_arguments(lib):
     assert s(p, p, p, p, 1, 4, 16, 2, 64, 1, float("nan"), None) == BAD
     assert s(p, p, p, None, 1, 4, 16, 2, 64, 1, 0.125, None) == BAD
     assert "NULL" in raw.ca2_last_error().decode()
+
+
+def test_toy_entry_points_reject_bad_arguments(lib):
+    raw = lib.load()
+    p = ctypes.c_void_p(4096)          # aligned, never dereferenced
+    BAD = lib.CA2_ERR_INVALID_ARG
+    assert raw.ca2_toy_temb_mod(p, 2, p, 7, 32, p, None) == BAD            # odd embedding width
+    assert raw.ca2_toy_temb_mod(p, 0, p, 8, 32, p, None) == BAD            # no frames
+    assert raw.ca2_toy_ln_mod(p, p, 64, 0, 40, 2, 16, 32, p, None) == BAD  # scale range past the mod row
+    assert raw.ca2_toy_ln_mod(None, p, 64, 0, 32, 2, 16, 32, p, None) == BAD
+    assert raw.ca2_toy_linear(p, 8, p, 16, None, 0, p, 16, 4, 16, 8, 2, None) == BAD   # act
+    assert raw.ca2_toy_linear(p, 4, p, 16, None, 0, p, 16, 4, 16, 8, 0, None) == BAD   # ldx < k
+    assert raw.ca2_toy_linear(p, 8, p, 16, p, 8, p, 16, 4, 16, 8, 0, None) == BAD      # ldr < n
+    assert raw.ca2_toy_linear(p, 8, None, 16, None, 0, p, 16, 4, 16, 8, 0, None) == BAD
