@@ -48,6 +48,11 @@ TEMPORAL_CASES = [
     ("bf16_d72_empty", shape_of(1, 16, 72, 16, 8, 25, 3, "bf16"), [], 1),
     ("bf16_d64", shape_of(1, 4, 64, 33, 8, 25, 3, "bf16"), [1, 8, 8, 8, 8], 8),
     ("bf16_d128", shape_of(1, 2, 128, 40, 8, 17, 3, "bf16"), [1, 8, 8, 8], 6),
+    # long queues: the ring wraps many times, head slot far from 0
+    ("bf16_d72_long_ring", shape_of(1, 2, 72, 8, 8, 201, 3, "bf16", 209), [1] + [8] * 30, 8),
+    ("f32_d16_long_ring", shape_of(1, 2, 16, 4, 4, 101, 1, "f32", 105), [1] + [4] * 40, 4),
+    # one spatial token per frame
+    ("bf16_d72_S1", shape_of(1, 3, 72, 1, 8, 25, 3, "bf16"), [1, 8, 8, 8], 8),
 ]
 
 
@@ -119,6 +124,14 @@ SPATIAL_CASES = [
     ("bf16_d72_tiny_tokens", shape_of(1, 3, 72, 9, 4, 9, 2, "bf16"), [1, 4], 4, 0),
     ("bf16_d64_prefix", shape_of(1, 4, 64, 192, 8, 25, 3, "bf16"), [1, 8], 8, 0),
     ("bf16_d128_prefix", shape_of(1, 2, 128, 100, 8, 25, 2, "bf16"), [1, 8], 4, 0),
+    # the largest prefix (P' = chunk - 1 = 15 frames, 16 key frames), filled and clamp-padded
+    ("bf16_d72_max_prefix", shape_of(1, 2, 72, 40, 16, 17, 15, "bf16", 33), [1, 16, 16], 16, 0),
+    ("bf16_d72_max_prefix_clamp", shape_of(1, 2, 72, 40, 16, 17, 15, "bf16", 33), [1], 16, 0),
+    ("bf16_d128_max_prefix", shape_of(1, 1, 128, 17, 16, 17, 15, "bf16", 33), [1, 16], 3, 0),
+    ("f32_d16_max_prefix", shape_of(1, 2, 16, 16, 16, 17, 15, "f32", 33), [1, 16], 5, 0),
+    # one token per frame: one real key per key frame, the rest of each tile masked
+    ("bf16_d64_S1", shape_of(1, 3, 64, 1, 4, 9, 2, "bf16"), [1, 4], 4, 0),
+    ("bf16_d64_S1_self", shape_of(1, 3, 64, 1, 4, 9, 2, "bf16"), [1, 4], 4, 1),
 ]
 
 
