@@ -185,11 +185,10 @@ def denoise_loop_graph(w: Workload, reps: int):
     return eager, graph
 
 
-def kernel_table(w: Workload, reps: int):
-    """Per-kernel average launch duration and roofline numbers for one workload."""
+def launchers(w: Workload):
+    """One launch of each attention kernel, rotating through the workload's
+    caches and Q/K/V sets as consecutive denoising calls do."""
     from causal_kv_cache_amd import ca2
-    sh = w.sh
-    n, pk, ps = sh["l"], sh["p_max"], sh["p_spatial"]
     sets, caches = w.sets, w.caches
     idx = [0]
 
@@ -209,6 +208,22 @@ def kernel_table(w: Workload, reps: int):
         c, _ = nxt()
         qc, kt, vt, ks, vs = w.clean
         c.ca2_spatial_attn(qc, ks, vs, w.out_s, mode=ca2.CA2_SPATIAL_SELF)
+
+    return {"spatial_prefix": k_spatial, "temporal": k_temporal, "spatial_self": k_spatial_self}
+
+
+def main_workload():
+    """The headline workload: the 256-token shape with 8 rotating caches and
+    one Q/K/V set per denoising call."""
+    return Workload(AR_STEP, T_DENOISE, seed=1234, n_caches=N_CACHES)
+
+
+def kernel_table(w: Workload, reps: int):
+    """Per-kernel average launch duration and roofline numbers for one workload."""
+    sh = w.sh
+    n, pk, ps = sh["l"], sh["p_max"], sh["p_spatial"]
+    fns = launchers(w)
+    k_spatial, k_temporal, k_spatial_self = fns["spatial_prefix"], fns["temporal"], fns["spatial_self"]
 
     rows = {}
     us = time_launches(k_spatial, reps)
@@ -422,13 +437,13 @@ def kernel_mode(kernel, workload, reps):
     if kernel == "qkv_proj":
         r = write_case(reps)
         return {"kernel": kernel, "workload": workload, **r["qkv_proj"]}
-    w = Workload(sh, 2, seed=11)
-    q, k, v = w.sets[0]
-    qc, kt, vt, ks, vs = w.clean
-    fn = {"spatial_prefix": lambda: w.cache.ca2_spatial_attn(q, k, v, w.out_s),
-          "spatial_self": lambda: w.cache.ca2_spatial_attn(qc, ks, vs, w.out_s, mode=ca2.CA2_SPATIAL_SELF),
-          "temporal": lambda: w.cache.ca2_temporal_attn(q, k, v, w.out_t),
-          "cache_write": lambda: w.cache.ca2_cache_write(kt, vt, ks, vs)}[kernel]
+    # the same buffers and rotation as the benchmark's per-kernel table
+    w = main_workload() if sh is AR_STEP else Workload(sh, 2, seed=99)
+    if kernel == "cache_write":
+        qc, kt, vt, ks, vs = w.clean
+        fn = lambda: w.cache.ca2_cache_write(kt, vt, ks, vs)
+    else:
+        fn = launchers(w)[kernel]
     us = time_launches(fn, reps)
     return {"kernel": kernel, "workload": workload, "reps": reps, "avg_us": round(us, 3)}
 
@@ -492,7 +507,7 @@ def main():
         print(json.dumps(kernel_mode(args.kernel, args.workload, args.reps)), flush=True)
         return
 
-    w = Workload(AR_STEP, T_DENOISE, seed=1234, n_caches=N_CACHES)
+    w = main_workload()
     for _ in range(args.warmup):
         w.ar_step()
     torch.cuda.synchronize()

@@ -117,6 +117,9 @@ def _stream(stream):
     if stream is not None:
         return ctypes.c_void_p(int(stream))
     import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:   # the current stream's handle without building a Stream object (~3 us per call)
+        return ctypes.c_void_p(raw(torch.cuda.current_device()))
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
