@@ -130,7 +130,7 @@ int64_t spatial_frame(int64_t fw, int32_t p, int32_t j) {
 
 extern "C" {
 
-const char* ca2_status_string(ca2_status s) {
+const char* ca2_status_string(int32_t s) {
   switch (s) {
     case CA2_OK: return "ok";
     case CA2_ERR_INVALID_ARG: return "invalid argument";

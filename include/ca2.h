@@ -257,8 +257,10 @@ ca2_status ca2_toy_linear(const float* x, int32_t ldx, const float* w, int32_t l
                           int32_t ldr, float* y, int32_t ldy, int32_t m, int32_t n, int32_t k,
                           int32_t act, void* stream);
 
-/* Static description of a status code. */
-const char* ca2_status_string(ca2_status status);
+/* Static description of a status code; any other integer gives
+ * "unknown status". Takes a plain integer so that codes from any caller,
+ * valid or not, are well defined. */
+const char* ca2_status_string(int32_t status);
 
 /* Detail of the last failing call on this thread ("" if none). */
 const char* ca2_last_error(void);
