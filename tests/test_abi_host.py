@@ -149,3 +149,35 @@ def test_toy_entry_points_reject_bad_arguments(lib):
     assert raw.ca2_toy_linear(p, 4, p, 16, None, 0, p, 16, 4, 16, 8, 0, None) == BAD   # ldx < k
     assert raw.ca2_toy_linear(p, 8, p, 16, p, 8, p, 16, 4, 16, 8, 0, None) == BAD      # ldr < n
     assert raw.ca2_toy_linear(p, 8, None, 16, None, 0, p, 16, 4, 16, 8, 0, None) == BAD
+
+
+def test_slot_maps_random_write_sequences(lib):
+    """Property check over random chunked write sequences: after every write the
+    library's ring and spatial slot maps (one counter and modular arithmetic)
+    equal the oracle's step-by-step simulations (deque with explicit eviction;
+    replace-oldest spatial slots), and the TPE indices of the next chunk are the
+    oracle's table walk."""
+    hypothesis = pytest.importorskip("hypothesis")
+    st = hypothesis.strategies
+
+    @hypothesis.settings(max_examples=150, deadline=None, derandomize=True)
+    @hypothesis.given(p_max=st.integers(1, 64), p_spatial=st.integers(0, 15),
+                      writes=st.lists(st.integers(1, 16), min_size=1, max_size=25),
+                      tpe_extra=st.integers(0, 9))
+    def check(p_max, p_spatial, writes, tpe_extra):
+        q, sc = TemporalQueue(p_max), SpatialCache(p_spatial)
+        fw = 0
+        for w in writes:
+            q.write(range(fw, fw + w))
+            if p_spatial:
+                sc.write(range(fw, fw + w))
+            fw += w
+            assert lib.ca2_ring_slot_map_raw(fw, p_max) == q.slot_map()
+            if p_spatial:
+                frames, slots = lib.ca2_spatial_slot_map_raw(fw, p_spatial)
+                assert frames == sc.logical_frames()
+                assert slots == [f % p_spatial for f in frames]
+            L = p_max + 16 + tpe_extra
+            assert lib.ca2_tpe_index_raw(fw, 16, L) == tpe_index_ref(fw, 16, L)
+
+    check()

@@ -215,3 +215,46 @@ def test_spatial_parity_every_launch_variant(ca2, monkeypatch, cfg, name, sh, wr
     torch.cuda.synchronize()
     ref = o.spatial_out(q, k, v, "prefix" if mode == 0 else "self")
     check_close(to_host(out), ref, "bf16", f"{name} cfg {cfg}")
+
+
+def _random_configs(n_cfg, seed):
+    """Seeded samples over the supported domain (both dtypes, every built
+    head_dim, ragged token counts, any chunk, queue and prefix size, partial
+    chunks, queues before and after eviction), with the spatial oracle's work
+    capped so the whole set runs in seconds."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n_cfg:
+        dtype = ["f32", "bf16"][g.integers(2)]
+        d = int(g.choice([16, 32, 64, 72, 128] if dtype == "f32" else [64, 72, 128]))
+        B, H, S = int(g.integers(1, 4)), int(g.integers(1, 6)), int(g.integers(1, 140))
+        l = int(g.integers(1, 17))
+        p_max = int(g.integers(1, 61))
+        p_spatial = int(g.integers(0, l))
+        writes = [1] + [int(g.integers(1, l + 1)) for _ in range(int(g.integers(0, 2 * p_max // l + 3)))]
+        n = int(g.integers(1, l + 1))
+        if B * n * H * S * S * (p_spatial + 1) * d > 1.5e9:
+            continue
+        sh = shape_of(B, H, d, S, l, p_max, p_spatial, dtype, p_max + l + int(g.integers(0, 6)))
+        out.append((f"rand{len(out)}_{dtype}_d{d}_B{B}H{H}S{S}_l{l}P{p_max}p{p_spatial}_w{sum(writes)}_n{n}",
+                    sh, writes, n))
+    return out
+
+
+RANDOM_CASES = _random_configs(40, 2024)
+
+
+@pytest.mark.parametrize("name,sh,writes,n", RANDOM_CASES, ids=[c[0] for c in RANDOM_CASES])
+def test_random_configs_both_kernels(ca2, name, sh, writes, n):
+    cache, o = fill(ca2, sh, 300, writes)
+    q, k, v = (o.noisy(x, 2, 11, n) for x in ("q", "k", "v"))
+    dq, dk, dv = (to_dev(x, sh["dtype"]) for x in (q, k, v))
+    out_t = empty_like_dev(q.shape, sh["dtype"])
+    out_s = empty_like_dev(q.shape, sh["dtype"])
+    cache.ca2_temporal_attn(dq, dk, dv, out_t)
+    cache.ca2_spatial_attn(dq, dk, dv, out_s, mode=0)
+    torch.cuda.synchronize()
+    check_close(to_host(out_t), temporal_attn_ref(q, k, v, o.ring_k, o.ring_v, o.queue.slot_map(), o.scale),
+                sh["dtype"], name + " temporal")
+    check_close(to_host(out_s), o.spatial_out(q, k, v, "prefix"), sh["dtype"], name + " spatial")
+    assert cache.ca2_cache_frame_ids()[0] == o.queue.frame_ids()
