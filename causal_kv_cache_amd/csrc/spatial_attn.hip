@@ -352,9 +352,13 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
   };
 
   // ---- prologue: tile 0 copied while Q is loaded, tiles 1..kStages-2 in flight, first chunk scored ----
+  // tiles 0 .. kStages-2 are all requested before the first wait; loads
+  // complete in issue order, so once only the younger tiles' copies are
+  // outstanding, Q (loaded first) and tile 0 have arrived
   issue_next();
-  wait_vmcnt<0>();   // Q and this wavefront's copies of tile 0 (the loop's waits count copies only)
-  for (int t = 1; t <= kStages - 2 && t < n_tiles; ++t) issue_next();
+  int pre = 0;
+  for (int t = 1; t <= kStages - 2 && t < n_tiles; ++t, ++pre) issue_next();
+  wait_tiles(pre);
   lds_barrier();
   f32x16 s0[QB], s1[QB];
   bf16x8v pf[QB][2];
