@@ -581,10 +581,11 @@ hipError_t launch_pipe_cfg(const SpatialArgs& a, hipStream_t s) {
 template <int D>
 hipError_t launch_mfma(const SpatialArgs& a, hipStream_t s) {
   // Large grids: 4 wavefronts x 64 queries (each K/V operand read from LDS
-  // feeds two MFMAs), two workgroups per CU, 4-stage ring. Below ~4 such
-  // workgroups per CU: 4 x 32 queries, which doubles the wavefronts in flight,
-  // with a 3-stage ring (fewer tiles in flight measured faster there: 18.5 vs
-  // 19.7 us at 256 tokens; 5 and 6 stages 23.5 us).
+  // feeds two MFMAs), two workgroups per CU. Below ~4 such workgroups per CU:
+  // 4 x 32 queries, which doubles the wavefronts in flight. Both use a 4-stage
+  // ring: at 256 tokens 3 stages time faster launched alone (18.5 vs 19.7 us)
+  // but slower in the denoising step that alternates with the temporal kernel
+  // (1.86 vs 1.80 ms per step); 5 and 6 stages take 23.5 us.
   // CA2_SPATIAL_CFG=1|2|3 forces 32 queries, 64 queries, or 8 wavefronts of
   // 32 queries x 2 key halves (two wavefronts per SIMD even at one workgroup
   // per CU; measured slower than 4 x 32 at the 256-token shape, kept
@@ -597,7 +598,7 @@ hipError_t launch_mfma(const SpatialArgs& a, hipStream_t s) {
     if (cfg == 2) return launch_pipe_cfg<D, 2, 4, 4, 1>(a, s);
   }
   if (cfg == 3) return launch_pipe_cfg<D, 1, 8, 4, 2>(a, s);
-  return launch_pipe_cfg<D, 1, 4, 3, 1>(a, s);
+  return launch_pipe_cfg<D, 1, 4, 4, 1>(a, s);
 }
 
 template <int D>
