@@ -1,6 +1,6 @@
 """Toy spatial-temporal transformer for the cache-sharing invariants (float64).
 
-Test infrastructure only (oracle-side; no GPU counterpart). Random weights, no
+Test infrastructure only: the reference for the GPU run of the same block. Random weights, no
 training. It exists to check, on a real stack of layers rather than on
 synthetic K/V, the two properties the Ca2-VDM pages rest the method on:
 
