@@ -147,19 +147,29 @@ class Workload:
         self.write_pass()
 
 
-def time_launches(fn, reps):
-    """Average duration of `fn` over `reps` back-to-back launches, from HIP
-    events recorded on the current (launch) stream."""
+def time_launches_stats(fn, reps, rounds=5):
+    """Per-launch duration of `fn` in microseconds: `rounds` blocks of `reps`
+    back-to-back launches, each block timed with HIP events recorded on the
+    current (launch) stream; returns (median, min, max) of the block averages."""
+    import statistics
     import torch
     fn()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps     # microseconds
+    vals = []
+    for _ in range(rounds):
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        vals.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return statistics.median(vals), min(vals), max(vals)
+
+
+def time_launches(fn, reps, rounds=5):
+    """Median per-launch duration (microseconds) over `rounds` blocks of `reps` launches."""
+    return time_launches_stats(fn, reps, rounds)[0]
 
 
 def denoise_loop_graph(w: Workload, reps: int):
@@ -226,18 +236,20 @@ def kernel_table(w: Workload, reps: int):
     k_spatial, k_temporal, k_spatial_self = fns["spatial_prefix"], fns["temporal"], fns["spatial_self"]
 
     rows = {}
-    us = time_launches(k_spatial, reps)
+    us, lo, hi = time_launches_stats(k_spatial, reps)
     fl = spatial_flops(sh, n, ps)
-    rows["spatial_attn_prefix"] = dict(us=us, flops=fl, bytes=spatial_bytes(sh, n, ps), bound="mfma",
-                                       achieved=fl / us / 1e6, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s")
-    us = time_launches(k_temporal, reps)
+    rows["spatial_attn_prefix"] = dict(us=us, us_min=lo, us_max=hi, flops=fl, bytes=spatial_bytes(sh, n, ps),
+                                       bound="mfma", achieved=fl / us / 1e6, peak=MFMA_BF16_PEAK_TFLOPS,
+                                       unit="TFLOP/s")
+    us, lo, hi = time_launches_stats(k_temporal, reps)
     by = temporal_bytes(sh, n, pk)
-    rows["temporal_attn"] = dict(us=us, flops=temporal_flops(sh, n, pk), bytes=by, bound="hbm",
-                                 achieved=by / us / 1e3, peak=HBM_PEAK_GBS, unit="GB/s")
-    us = time_launches(k_spatial_self, max(4, reps // 4))
+    rows["temporal_attn"] = dict(us=us, us_min=lo, us_max=hi, flops=temporal_flops(sh, n, pk), bytes=by,
+                                 bound="hbm", achieved=by / us / 1e3, peak=HBM_PEAK_GBS, unit="GB/s")
+    us, lo, hi = time_launches_stats(k_spatial_self, max(4, reps // 4))
     fl = spatial_flops(sh, n, 0)
-    rows["spatial_attn_self"] = dict(us=us, flops=fl, bytes=spatial_bytes(sh, n, 0), bound="mfma",
-                                     achieved=fl / us / 1e6, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s")
+    rows["spatial_attn_self"] = dict(us=us, us_min=lo, us_max=hi, flops=fl, bytes=spatial_bytes(sh, n, 0),
+                                     bound="mfma", achieved=fl / us / 1e6, peak=MFMA_BF16_PEAK_TFLOPS,
+                                     unit="TFLOP/s")
     for r in rows.values():
         r["frac"] = r["achieved"] / r["peak"]
     return rows
@@ -275,7 +287,7 @@ def traffic_for(kernel, workload):
     return e.get("hbm_bytes_per_launch")
 
 
-def write_case(reps):
+def write_case(reps, rounds=5):
     """Cache-writing stage at write_b4: QKV projection of the clean chunk
     (B*l*S x 1152 -> 3 x 1152) and the cache write of its K/V."""
     import torch
@@ -290,8 +302,8 @@ def write_case(reps):
     q, k, v = (torch.empty((m, c), dtype=torch.bfloat16, device="cuda") for _ in range(3))
     w = Workload(sh, 1, seed=8)
     kk, vv = k.view(B, l, S, H, d), v.view(B, l, S, H, d)
-    us_p = time_launches(lambda: ca2.ca2_qkv_proj(x, wgt, q, k, v), reps)
-    us_w = time_launches(lambda: w.cache.ca2_cache_write(kk, vv, kk, vv), reps)
+    us_p = time_launches(lambda: ca2.ca2_qkv_proj(x, wgt, q, k, v), reps, rounds)
+    us_w = time_launches(lambda: w.cache.ca2_cache_write(kk, vv, kk, vv), reps, rounds)
     fl = 2 * m * c * 3 * c
     wb = write_bytes(sh, l)
     shared = w.cache.ca2_cache_info_get()["bytes_resident"]
@@ -435,7 +447,7 @@ def kernel_mode(kernel, workload, reps):
     from causal_kv_cache_amd import ca2
     sh = WORKLOADS[workload]
     if kernel == "qkv_proj":
-        r = write_case(reps)
+        r = write_case(reps, rounds=1)
         return {"kernel": kernel, "workload": workload, **r["qkv_proj"]}
     # the same buffers and rotation as the benchmark's per-kernel table
     w = main_workload() if sh is AR_STEP else Workload(sh, 2, seed=99)
@@ -444,7 +456,7 @@ def kernel_mode(kernel, workload, reps):
         fn = lambda: w.cache.ca2_cache_write(kt, vt, ks, vs)
     else:
         fn = launchers(w)[kernel]
-    us = time_launches(fn, reps)
+    us = time_launches(fn, reps, rounds=1)      # exactly 1 + reps launches, all traced
     return {"kernel": kernel, "workload": workload, "reps": reps, "avg_us": round(us, 3)}
 
 
