@@ -198,9 +198,21 @@ def test_large_b8_s1024_sampled(ca2):
         check_close(to_host(os_)[b:b + 1, :, toks], ref_s, "bf16", f"large spatial b={b}")
 
 
+FULL_TILE_CASES = [
+    # token counts that are whole 64-key tiles (the exact-count copy waits)
+    ("bf16_d72_S64_prefix", shape_of(2, 3, 72, 64, 8, 25, 3, "bf16"), [1, 8, 8], 8, 0),
+    ("bf16_d72_S256_prefix", shape_of(1, 2, 72, 256, 8, 25, 3, "bf16"), [1, 8, 8, 8], 8, 0),
+    ("bf16_d72_S512_clamp", shape_of(1, 1, 72, 512, 4, 9, 3, "bf16"), [1], 3, 0),
+    ("bf16_d72_S128_self", shape_of(1, 3, 72, 128, 8, 25, 3, "bf16"), [1, 8], 5, 1),
+    ("bf16_d64_S192_prefix", shape_of(1, 2, 64, 192, 8, 25, 2, "bf16"), [1, 8, 8], 6, 0),
+    ("bf16_d72_S1024_p1", shape_of(1, 1, 72, 1024, 4, 9, 1, "bf16"), [1, 4], 2, 0),
+]
+
+
 @pytest.mark.parametrize("cfg", ["1", "2", "3"])
-@pytest.mark.parametrize("name,sh,writes,n,mode", [c for c in SPATIAL_CASES if c[1]["dtype"] == "bf16"],
-                         ids=[c[0] for c in SPATIAL_CASES if c[1]["dtype"] == "bf16"])
+@pytest.mark.parametrize("name,sh,writes,n,mode",
+                         [c for c in SPATIAL_CASES if c[1]["dtype"] == "bf16"] + FULL_TILE_CASES,
+                         ids=[c[0] for c in SPATIAL_CASES if c[1]["dtype"] == "bf16"] + [c[0] for c in FULL_TILE_CASES])
 def test_spatial_parity_every_launch_variant(ca2, monkeypatch, cfg, name, sh, writes, n, mode):
     """Every bf16 launch variant (4 wavefronts x 32 queries, 4 x 64 queries,
     8 wavefronts = 4 x 32 queries x 2 key halves) against the oracle,
