@@ -16,6 +16,10 @@
  * one chunk's spatial K/V, overwritten every autoregressive step). The cache is
  * read by every denoising call and written only by ca2_cache_write, so one
  * copy serves all T denoising steps ([notes] key design 2, cache sharing).
+ * Beside the cache object: the QKV projection of the cache-writing pass,
+ * cache-less attention over T frames (the recompute baseline the cache
+ * removes), and the pieces of a small random-weight block used to check the
+ * cache end to end (ca2_toy_*).
  *
  * Conventions (all entry points):
  *   - Layout of every activation tensor: [B][n][S][H][d] contiguous
