@@ -1,0 +1,74 @@
+"""A cache whose ring spans more than 4 GiB (64x64-latent frames of 4096
+tokens x 16 heads x 72, P_max = 480 queued frames: 9.1 GB of K/V), filled
+past eviction and wrap, so the cache write and both attention kernels run
+with byte offsets beyond 32 bits. Inputs are seeded torch draws made on the
+device; the oracle checks sampled rows (temporal) and sampled queries
+(spatial) from host copies of exactly those inputs. bf16 bar: max-abs 2e-2."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import temporal_attn_ref, spatial_attn_ref
+from gpu_util import to_host, check_close
+
+pytestmark = pytest.mark.gpu
+
+B, H, d, S, L, P_MAX, P_SP = 1, 16, 72, 4096, 8, 480, 3
+
+
+def test_ring_beyond_4gib(ca2):
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20260)
+    cache = ca2.Cache(B, H, d, S, L, P_MAX, P_SP, P_MAX + L, "bf16")
+    assert cache.ca2_cache_info_get()["bytes_resident"] > 2 ** 33
+    rng = np.random.default_rng(7)
+    rows = [(int(s), int(h)) for s, h in zip(rng.integers(0, S, 24), rng.integers(0, H, 24))]
+    s_idx = torch.tensor([r[0] for r in rows], device="cuda")
+    h_idx = torch.tensor([r[1] for r in rows], device="cuda")
+
+    def draw(n):
+        return [torch.randn((B, n, S, H, d), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(4)]
+
+    def rows_of(t):          # [B][n][S][H][d] -> host [B][n][R][d] at the sampled (s, h)
+        return to_host(t[:, :, s_idx, h_idx])
+
+    kt_hist, vt_hist = [], []  # sampled temporal K/V of every written frame, in order
+    spatial_last = None        # full spatial K/V of the last chunk (the buffer holds its last P' frames)
+    for n in [1] + [L] * 60:   # 481 frames: the queue holds frames 1..480, the ring has wrapped
+        kt, vt, ks, vs = draw(n)
+        cache.ca2_cache_write(kt, vt, ks, vs)
+        kt_hist.append(rows_of(kt))
+        vt_hist.append(rows_of(vt))
+        spatial_last = (ks, vs)
+    torch.cuda.synchronize()
+    info = cache.ca2_cache_info_get()
+    assert info["p_k"] == P_MAX and info["frames_written"] == 481
+    q, k, v = (torch.randn((B, L, S, H, d), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(3))
+    out_t = torch.empty_like(q)
+    out_s = torch.empty_like(q)
+    cache.ca2_temporal_attn(q, k, v, out_t)
+    cache.ca2_spatial_attn(q, k, v, out_s)
+    torch.cuda.synchronize()
+
+    # temporal: sampled rows against the oracle over the queued frames 1..480
+    kq = np.concatenate(kt_hist, axis=1)[:, 1:]            # [B][480][R][d]
+    vq = np.concatenate(vt_hist, axis=1)[:, 1:]
+    R = len(rows)
+    ring_k = kq.reshape(B, P_MAX, R, 1, d)                  # the queue in logical order, one row per "token"
+    ring_v = vq.reshape(B, P_MAX, R, 1, d)
+    ref = temporal_attn_ref(rows_of(q).reshape(B, L, R, 1, d), rows_of(k).reshape(B, L, R, 1, d),
+                            rows_of(v).reshape(B, L, R, 1, d), ring_k, ring_v, list(range(P_MAX)), d ** -0.5)
+    check_close(rows_of(out_t).reshape(B, L, R, 1, d), ref, "bf16", "temporal, 9.1 GB ring")
+
+    # spatial: sampled queries of two (frame, head) pairs; prefix = the last P' clean frames
+    ks, vs = spatial_last
+    ks_h, vs_h = to_host(ks[:, -P_SP:]), to_host(vs[:, -P_SP:])   # frames 478..480, oldest first
+    qh, kh, vh, oh = to_host(q), to_host(k), to_host(v), to_host(out_s)
+    toks = np.sort(rng.choice(S, 48, replace=False))
+    for f, h in ((0, 3), (7, 15)):
+        sl = (slice(None), slice(f, f + 1))
+        ref_s = spatial_attn_ref(qh[sl][:, :, toks][:, :, :, h:h + 1], kh[sl][:, :, :, h:h + 1],
+                                 vh[sl][:, :, :, h:h + 1], ks_h[:, :, :, h:h + 1], vs_h[:, :, :, h:h + 1],
+                                 list(range(P_SP)), d ** -0.5, "prefix")
+        check_close(oh[sl][:, :, toks][:, :, :, h:h + 1], ref_s, "bf16", f"spatial frame {f} head {h}")
+    cache.close()
