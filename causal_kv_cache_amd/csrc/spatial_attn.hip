@@ -229,8 +229,17 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
   uint64_t pslots = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) pslots |= (uint64_t)(a.prefix_slot[i] & 15) << (4 * i);
-  asm volatile("" : "+s"(sp_k), "+s"(sp_v), "+s"(fk), "+s"(fv), "+s"(pslots));
+  // key frames are streamed prefix frames first (shared by every frame of the
+  // chunk, so likely already in L2) and the frame's own keys last
+  const unsigned char* own_k = fk;
+  const unsigned char* own_v = fv;
+  asm volatile("" : "+s"(sp_k), "+s"(sp_v), "+s"(fk), "+s"(fv), "+s"(pslots), "+s"(own_k), "+s"(own_v));
   const int64_t pbase = ((int64_t)b * a.p_slots * S) * tok_stride * 2 + (int64_t)head * D * 2;
+  if (a.n_prefix > 0) {
+    const int64_t off0 = pbase + (int64_t)(pslots & 15) * S * tok_stride * 2;
+    fk = sp_k + off0;
+    fv = sp_v + off0;
+  }
   const int64_t tile_bytes = (int64_t)kBN * tok_stride * 2;
   const int tiles_per_frame = (S + kBN - 1) / kBN;
   const int n_tiles = (1 + a.n_prefix) * tiles_per_frame;
@@ -255,10 +264,15 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))
     if (t0_c >= S) {
       t0_c = 0;
       ++kf_c;
-      const int slot = (int)((pslots >> (4 * (kf_c - 1))) & 15);
-      const int64_t off = pbase + (int64_t)slot * S * tok_stride * 2;
-      fk = sp_k + off;
-      fv = sp_v + off;
+      if (kf_c < a.n_prefix) {
+        const int slot = (int)((pslots >> (4 * kf_c)) & 15);
+        const int64_t off = pbase + (int64_t)slot * S * tok_stride * 2;
+        fk = sp_k + off;
+        fv = sp_v + off;
+      } else {
+        fk = own_k;
+        fv = own_v;
+      }
     }
     st_c = st_c == kStages - 1 ? 0 : st_c + 1;
   };
