@@ -18,6 +18,11 @@ synthetic K/V, the two properties the Ca2-VDM pages rest the method on:
 Block = spatial attention (prefix-enhanced for targets, self for clean frames)
 -> causal temporal attention -> MLP, each pre-normalised and modulated by the
 frame's own timestep embedding (adaLN style: shift and scale).
+
+The layer forms (layer norm, tanh-GELU, sinusoidal timestep embedding,
+shift/scale modulation) are textbook choices: the pages do not specify the
+backbone, so those definitions are parity unpinned; the two cache properties
+above are what the tests pin.
 """
 from __future__ import annotations
 
