@@ -456,42 +456,43 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
     }
   }
 
-  // merge the wavefronts of a split key range
+  // merge the wavefronts of a split key range: query qq of every lane is
+  // merged and stored by wave qq % splits; the other waves hand over their
+  // partial state for it through LDS (slot per (query, writer))
+  constexpr int SLOT = (DPL + 2) * 64;
+  unsigned char* ob = static_cast<unsigned char*>(a.out);
   if (splits > 1) {
-    constexpr int PER_LANE = kQPL * (DPL + 2);
-    if (wave > 0) {
-      float* dst = merge_lds + (wave - 1) * 64 * PER_LANE + lane;
 #pragma unroll
-      for (int qq = 0; qq < kQPL; ++qq) {
-        dst[(qq * (DPL + 2)) * 64] = m[qq];
-        dst[(qq * (DPL + 2) + 1) * 64] = l[qq];
+    for (int qq = 0; qq < kQPL; ++qq) {
+      const int own = qq % splits;
+      if (own != wave) {
+        float* dst = merge_lds + (qq * (splits - 1) + (wave < own ? wave : wave - 1)) * SLOT + lane;
+        dst[0] = m[qq];
+        dst[64] = l[qq];
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) dst[(qq * (DPL + 2) + 2 + e) * 64] = acc[qq][e];
+        for (int e = 0; e < DPL; ++e) dst[(2 + e) * 64] = acc[qq][e];
       }
     }
     __syncthreads();
-    if (wave > 0) return;
-    for (int w = 1; w < splits; ++w) {
-      const float* src = merge_lds + (w - 1) * 64 * PER_LANE + lane;
 #pragma unroll
-      for (int qq = 0; qq < kQPL; ++qq) {
-        const float mw = src[(qq * (DPL + 2)) * 64];
+    for (int qq = 0; qq < kQPL; ++qq) {
+      if (qq % splits != wave) continue;
+      for (int w = 0; w < splits - 1; ++w) {
+        const float* src = merge_lds + (qq * (splits - 1) + w) * SLOT + lane;
+        const float mw = src[0];
         const float mn = fmaxf(m[qq], mw);
         const float s0 = fast_exp2(m[qq] - mn);
         const float s1 = fast_exp2(mw - mn);
         m[qq] = mn;
-        l[qq] = l[qq] * s0 + src[(qq * (DPL + 2) + 1) * 64] * s1;
+        l[qq] = l[qq] * s0 + src[64] * s1;
 #pragma unroll
-        for (int e = 0; e < DPL; ++e)
-          acc[qq][e] = acc[qq][e] * s0 + src[(qq * (DPL + 2) + 2 + e) * 64] * s1;
+        for (int e = 0; e < DPL; ++e) acc[qq][e] = acc[qq][e] * s0 + src[(2 + e) * 64] * s1;
       }
     }
   }
-
-  unsigned char* ob = static_cast<unsigned char*>(a.out);
 #pragma unroll
   for (int qq = 0; qq < kQPL; ++qq) {
-    if (!qok[qq]) continue;
+    if (!qok[qq] || qq % splits != wave) continue;
     const int qi = q0 + qg * kQPL + qq;
     const float inv = 1.f / l[qq];
     float o[DPL];
