@@ -37,13 +37,13 @@ from .cache import (
     tpe_index_ref,
     bytes_resident_ref,
 )
-from .projection import qkv_proj_ref
+from .projection import qkv_proj_ref, qkv_proj_tpe_ref
 from .rollout import ar_schedule, RolloutOracle
 
 __all__ = [
     "softmax_rows", "temporal_attn_ref", "spatial_attn_ref",
     "spatial_attn_selfrepeat_ref", "masked_causal_attn_ref",
     "full_recompute_temporal_ref", "bidirectional_temporal_ref", "TemporalQueue", "SpatialCache",
-    "tpe_index_ref", "bytes_resident_ref", "qkv_proj_ref", "ar_schedule",
+    "tpe_index_ref", "bytes_resident_ref", "qkv_proj_ref", "qkv_proj_tpe_ref", "ar_schedule",
     "RolloutOracle",
 ]

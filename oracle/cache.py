@@ -16,19 +16,26 @@ class TemporalQueue:
     once it reaches P_max the oldest entries leave the queue, so its length
     stays P_max.
 
-    Physical placement: a new frame goes to slot (head + length) mod P_max,
-    i.e. right after the newest entry; when the queue then holds more than
-    P_max ids the oldest is dropped and ``head`` advances by one. The slot of
-    logical position j is (head + j) mod P_max.
+    Physical placement over ``slots`` physical slots (P_max unless more are
+    asked for): a new frame goes to slot (head + length) mod slots, i.e.
+    right after the newest entry; when the queue then holds more than P_max
+    ids the oldest is dropped and ``head`` advances by one. The slot of
+    logical position j is (head + j) mod slots. With slots >= P_max + n, the
+    n frames of a write land in slots that held no queued frame before it, so
+    they can be filled before the queue moves on.
 
-    Pinned by brute force (a plain list that keeps the last P_max ids) and by
-    the invariant "queue == last min(N, P_max) frame ids".
+    Pinned by brute force (a plain list that keeps the last P_max ids), by
+    the invariant "queue == last min(N, P_max) frame ids" and, for the
+    placement, by a last-writer-wins table of which frame each slot holds.
     """
 
-    def __init__(self, p_max: int):
+    def __init__(self, p_max: int, slots: int | None = None):
         if p_max < 1:
             raise ValueError("p_max must be >= 1")
         self.p_max = p_max
+        self.slots = p_max if slots is None else int(slots)
+        if self.slots < p_max:
+            raise ValueError("slots must be >= p_max")
         self.ids = deque()
         self.head = 0
 
@@ -41,12 +48,12 @@ class TemporalQueue:
         physical slot each written frame landed in."""
         slots = []
         for f in frame_ids:
-            slot = (self.head + len(self.ids)) % self.p_max
+            slot = (self.head + len(self.ids)) % self.slots
             self.ids.append(int(f))
             slots.append(slot)
             while len(self.ids) > self.p_max:
                 self.ids.popleft()
-                self.head = (self.head + 1) % self.p_max
+                self.head = (self.head + 1) % self.slots
         return slots
 
     def frame_ids(self):
@@ -54,7 +61,7 @@ class TemporalQueue:
 
     def slot_map(self):
         """Physical slot of each logical position, oldest first."""
-        return [(self.head + j) % self.p_max for j in range(len(self.ids))]
+        return [(self.head + j) % self.slots for j in range(len(self.ids))]
 
 
 class SpatialCache:

@@ -216,3 +216,37 @@ def check_bidirectional_last_frame_is_causal(bidir_impl, causal_impl, B=1, T=6, 
     last = float(np.max(np.abs(got[:, -1] - causal[:, -1])))
     first_differs = float(np.max(np.abs(got[:, 0] - causal[:, 0]))) > 1e-3
     return last if first_differs else float("inf")
+
+
+# ---------------------------------------------------------------------------
+# QKV projection with the cyclic TPE row (pins for qkv_proj_tpe_ref-shaped
+# implementations: impl(x, w, tpe_rows, first_frame, n_frames, tokens))
+# ---------------------------------------------------------------------------
+# frames 11..14 with a table of 13 rows wrap after frame 12: indices written
+# out by hand, not computed
+_TPE_FIRST, _TPE_N, _TPE_L, _TPE_IDX = 11, 4, 13, [11, 12, 0, 1]
+
+
+def check_tpe_proj_zero_input(impl, B=2, S=3, C_in=5, C=2, seed=21):
+    """x = 0: every output row is exactly its frame's table row."""
+    g = np.random.default_rng(seed)
+    w = g.standard_normal((3 * C, C_in))
+    rows = g.standard_normal((_TPE_L, 3 * C))
+    x = np.zeros((B * _TPE_N * S, C_in))
+    y = np.concatenate(impl(x, w, rows, _TPE_FIRST, _TPE_N, S), 1)
+    want = np.concatenate([np.repeat(rows[_TPE_IDX], S, 0)] * B, 0)
+    return float(np.max(np.abs(y - want)))
+
+
+def check_tpe_proj_distributive(impl, B=2, S=3, C_in=6, C=3, seed=22):
+    """Table rows built as e W^T: the result equals projecting x + e[index]
+    (the embedding added to the tokens first)."""
+    from oracle import qkv_proj_ref
+    g = np.random.default_rng(seed)
+    w = g.standard_normal((3 * C, C_in))
+    e = g.standard_normal((_TPE_L, C_in))
+    x = g.standard_normal((B * _TPE_N * S, C_in))
+    per_row = np.concatenate([np.repeat(e[_TPE_IDX], S, 0)] * B, 0)
+    want = np.concatenate(qkv_proj_ref(x + per_row, w), 1)
+    got = np.concatenate(impl(x, w, e @ w.T, _TPE_FIRST, _TPE_N, S), 1)
+    return float(np.max(np.abs(got - want)))

@@ -129,3 +129,51 @@ def test_bytes_resident_write_case():
     b = bytes_resident_ref(4, 256, 16, 72, 41, 3, 2)
     assert b == 193_462_272 + 14_155_776 == 207_618_048
     assert 50 * b == 10_380_902_400
+
+
+def _brute_force_ring_slots(p_max, nslots, total):
+    """A physical array of nslots >= P_max slots written frame by frame: each
+    new frame takes the lowest empty slot, else overwrites the slot holding
+    the oldest frame physically present. The queue is the newest P_max of the
+    frames present. Returns (queued ids in age order, their slots)."""
+    slots = [None] * nslots
+    for frame in range(total):
+        if None in slots:
+            s = slots.index(None)
+        else:
+            s = min(range(nslots), key=lambda i: slots[i])
+        slots[s] = frame
+    held = sorted(f for f in slots if f is not None)[-p_max:]
+    return held, [slots.index(f) for f in held]
+
+
+@pytest.mark.parametrize("p_max,l,writes", [
+    (9, 4, [1, 4, 4, 4, 4, 4, 4]),
+    (41, 8, [1] + [8] * 12),
+    (25, 8, [1, 8, 8, 8, 8, 3, 8]),
+    (1, 2, [1, 2, 1, 2, 2]),
+])
+def test_queue_with_staging_slots(p_max, l, writes):
+    """P_max + l physical slots: placement equals the brute-force ring, and the
+    slots a write fills held no queued frame before the write, so the new
+    frames can be stored before the queue moves on."""
+    q = TemporalQueue(p_max, slots=p_max + l)
+    total = 0
+    for w in writes:
+        before = set(q.slot_map())
+        landed = q.write(range(total, total + w))
+        total += w
+        assert not before & set(landed)
+        assert len(set(landed)) == len(landed)
+        ids, slots = _brute_force_ring_slots(p_max, p_max + l, total)
+        assert q.frame_ids() == ids == list(range(max(0, total - p_max), total))
+        assert q.slot_map() == slots
+
+
+def test_queue_without_staging_slots_overwrites_queued_frames():
+    """With exactly P_max slots a full queue's write lands on frames it still
+    holds before the write (why a staged write needs the extra slots)."""
+    q = TemporalQueue(5)
+    q.write(range(5))
+    before = set(q.slot_map())
+    assert before & set(q.write(range(5, 7)))

@@ -37,3 +37,57 @@ def test_linearity():
     a = np.concatenate(qkv_proj_ref(2 * x1 - 3 * x2, w), 1)
     b = 2 * np.concatenate(qkv_proj_ref(x1, w), 1) - 3 * np.concatenate(qkv_proj_ref(x2, w), 1)
     assert np.max(np.abs(a - b)) <= 1e-12
+
+
+# --- projection with the cyclic TPE row --------------------------------------
+import pytest  # noqa: E402
+
+import pins  # noqa: E402
+from oracle import qkv_proj_tpe_ref  # noqa: E402
+from oracle.projection import qkv_proj_ref as _plain  # noqa: E402
+
+
+def test_tpe_zero_input_gives_table_rows():
+    assert pins.check_tpe_proj_zero_input(qkv_proj_tpe_ref) == 0.0
+
+
+def test_tpe_equals_projecting_embedded_tokens():
+    assert pins.check_tpe_proj_distributive(qkv_proj_tpe_ref) <= 1e-12
+
+
+def _tpe_mutant(kind):
+    def impl(x, w, rows, first, n, S):
+        x = np.asarray(x, np.float64)
+        y = np.concatenate(_plain(x, w), 1)
+        L = rows.shape[0]
+        for r in range(x.shape[0]):
+            f = (r // S) % n
+            if kind == "no_add":
+                continue
+            if kind == "off_by_one":
+                i = (first + f + 1) % L
+            elif kind == "no_wrap":
+                i = min(first + f, L - 1)
+            elif kind == "frame_ignores_batch":
+                i = (first + min(r // S, n - 1)) % L
+            elif kind == "token_index":
+                i = (first + (r % S)) % L
+            else:
+                i = (first + f) % L
+            y[r] += rows[i] if kind != "k_only" else np.concatenate([0 * rows[i][:y.shape[1] // 3],
+                                                                     rows[i][y.shape[1] // 3:]])
+        C = y.shape[1] // 3
+        return y[:, :C], y[:, C:2 * C], y[:, 2 * C:]
+    return impl
+
+
+@pytest.mark.parametrize("kind", ["no_add", "off_by_one", "no_wrap", "frame_ignores_batch", "token_index",
+                                  "k_only"])
+def test_tpe_mutants_fail_a_pin(kind):
+    m = _tpe_mutant(kind)
+    assert pins.check_tpe_proj_zero_input(m) > 1e-9 or pins.check_tpe_proj_distributive(m) > 1e-9
+
+
+def test_tpe_mutant_harness_passes_unmutated():
+    m = _tpe_mutant("none")
+    assert pins.check_tpe_proj_zero_input(m) == 0.0 and pins.check_tpe_proj_distributive(m) <= 1e-12
