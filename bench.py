@@ -20,7 +20,7 @@ all conditional frames at every call), and the CPU oracle timed on a bounded
 sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-large] [--no-rollout]
-       python bench.py --kernel {spatial_prefix,temporal,spatial_self,cache_write,qkv_proj}
+       python bench.py --kernel {spatial_prefix,temporal,spatial_self,cache_write,qkv_proj,qkv_proj_stage}
                        --workload {ar_step_s256,large_b8_s1024,write_b4} --reps R   (one kernel, for profilers)
 """
 from __future__ import annotations
@@ -49,7 +49,7 @@ ROLLOUT = dict(name="rollout_80f", B=1, H=16, d=72, S=256, l=8, p_max=41, p_spat
 ROLLOUT_FRAMES = 80
 ROLLOUT_LAYERS = 8   # attention layers per model call in the rollout comparison
 WORKLOADS = {w["name"]: w for w in (AR_STEP, LARGE, WRITE)}
-KERNELS = ("spatial_prefix", "temporal", "spatial_self", "cache_write", "qkv_proj")
+KERNELS = ("spatial_prefix", "temporal", "spatial_self", "cache_write", "qkv_proj", "qkv_proj_stage")
 
 
 # ----------------------------------------------------------------------------
@@ -256,7 +256,8 @@ def kernel_table(w: Workload, reps: int):
 
 
 SOURCES = {"spatial_prefix": "spatial_attn.hip", "spatial_self": "spatial_attn.hip",
-           "temporal": "temporal_attn.hip", "cache_write": "cache_write.hip", "qkv_proj": "qkv_proj.hip"}
+           "temporal": "temporal_attn.hip", "cache_write": "cache_write.hip", "qkv_proj": "qkv_proj.hip",
+           "qkv_proj_stage": "qkv_proj.hip"}
 
 
 def source_hash(kernel):
@@ -287,9 +288,14 @@ def traffic_for(kernel, workload):
     return e.get("hbm_bytes_per_launch")
 
 
-def write_case(reps, rounds=5):
+def write_case(reps, rounds=5, only=None):
     """Cache-writing stage at write_b4: QKV projection of the clean chunk
-    (B*l*S x 1152 -> 3 x 1152) and the cache write of its K/V."""
+    (B*l*S x 1152 -> 3 x 1152) and the cache write of its K/V, then the same
+    stage fused (ca2_qkv_proj_stage on a cache with staging slots: Q to the
+    caller, K/V straight into the ring slots and the spatial buffer, the
+    projected TPE row added, and the commit). The queue starts full, so every
+    write evicts. only = "qkv_proj" or "qkv_proj_stage" times just that one
+    (profiling)."""
     import torch
     from causal_kv_cache_amd import ca2
     sh = WRITE
@@ -302,9 +308,28 @@ def write_case(reps, rounds=5):
     q, k, v = (torch.empty((m, c), dtype=torch.bfloat16, device="cuda") for _ in range(3))
     w = Workload(sh, 1, seed=8)
     kk, vv = k.view(B, l, S, H, d), v.view(B, l, S, H, d)
-    us_p = time_launches(lambda: ca2.ca2_qkv_proj(x, wgt, q, k, v), reps, rounds)
-    us_w = time_launches(lambda: w.cache.ca2_cache_write(kk, vv, kk, vv), reps, rounds)
     fl = 2 * m * c * 3 * c
+    # the staged cache, filled to P_max
+    st = ca2.Cache(B, H, d, S, l, sh["p_max"], sh["p_spatial"], sh["tpe_len"], "bf16", staged=True)
+    f1 = kk[:, :1].contiguous()
+    st.ca2_cache_write(f1, f1, f1, f1)
+    while st.ca2_cache_info_get()["p_k"] < sh["p_max"]:
+        st.ca2_cache_write(kk, vv, kk, vv)
+    tpe = (torch.randn((sh["tpe_len"], 3 * c), generator=gen, device="cuda") * 0.02).contiguous()
+    x4, q5 = x.view(B, l, S, c), q.view(B, l, S, H, d)
+
+    def fused():
+        st.ca2_qkv_proj_stage(x4, wgt, tpe, q5, None, None)
+        st.ca2_cache_commit()
+
+    if only == "qkv_proj_stage":
+        us_f = time_launches(fused, reps, rounds)
+        return {"qkv_proj_stage": {"us": round(us_f, 3), "flops": fl}}
+    us_p = time_launches(lambda: ca2.ca2_qkv_proj(x, wgt, q, k, v), reps, rounds)
+    if only == "qkv_proj":
+        return {"qkv_proj": {"us": round(us_p, 3), "flops": fl}}
+    us_w = time_launches(lambda: w.cache.ca2_cache_write(kk, vv, kk, vv), reps, rounds)
+    us_f = time_launches(fused, reps, rounds)
     wb = write_bytes(sh, l)
     shared = w.cache.ca2_cache_info_get()["bytes_resident"]
     return {"workload": sh["name"],
@@ -314,7 +339,12 @@ def write_case(reps, rounds=5):
             "cache_write": {"us": round(us_w, 3), "bytes": wb, "achieved_gbs": round(wb / us_w / 1e3, 1),
                             "frac_hbm": round(wb / us_w / 1e3 / HBM_PEAK_GBS, 4),
                             "traffic": traffic_for("cache_write", sh["name"])},
-            "bytes_resident": {"shared_cache": shared, "per_timestep_copies_T50": 50 * shared}}
+            "qkv_proj_stage_fused": {"us": round(us_f, 3), "unfused_us": round(us_p + us_w, 3),
+                                     "achieved_tflops": round(fl / us_f / 1e6, 2),
+                                     "frac_mfma": round(fl / us_f / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                                     "traffic": traffic_for("qkv_proj_stage", sh["name"])},
+            "bytes_resident": {"shared_cache": shared, "per_timestep_copies_T50": 50 * shared,
+                               "with_staging_slots": st.ca2_cache_info_get()["bytes_resident"]}}
 
 
 def recompute_bytes(sh, T, eb=2):
@@ -446,9 +476,9 @@ def kernel_mode(kernel, workload, reps):
     import torch
     from causal_kv_cache_amd import ca2
     sh = WORKLOADS[workload]
-    if kernel == "qkv_proj":
-        r = write_case(reps, rounds=1)
-        return {"kernel": kernel, "workload": workload, **r["qkv_proj"]}
+    if kernel in ("qkv_proj", "qkv_proj_stage"):
+        r = write_case(reps, rounds=1, only=kernel)
+        return {"kernel": kernel, "workload": workload, **r[kernel]}
     # the same buffers and rotation as the benchmark's per-kernel table
     w = main_workload() if sh is AR_STEP else Workload(sh, 2, seed=99)
     if kernel == "cache_write":

@@ -24,6 +24,8 @@ CA2_F32 = 0
 CA2_BF16 = 1
 CA2_SPATIAL_PREFIX = 0
 CA2_SPATIAL_SELF = 1
+CA2_STAGE_RING = 1
+CA2_STAGE_SPATIAL = 2
 
 _DTYPES = {"f32": CA2_F32, "bf16": CA2_BF16}
 
@@ -38,8 +40,9 @@ class Ca2Config(ctypes.Structure):
 
 class Ca2CacheInfo(ctypes.Structure):
     _fields_ = [("p_k", ctypes.c_int32), ("head_slot", ctypes.c_int32),
-                ("spatial_frames", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("frames_written", ctypes.c_int64), ("bytes_resident", ctypes.c_uint64)]
+                ("spatial_frames", ctypes.c_int32), ("staged_frames", ctypes.c_int32),
+                ("frames_written", ctypes.c_int64), ("bytes_resident", ctypes.c_uint64),
+                ("ring_slots", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 # name -> (restype, argtypes)
@@ -48,6 +51,9 @@ _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _SIGS = {
     "ca2_cache_create": (_I32, [ctypes.POINTER(Ca2Config), ctypes.POINTER(_P)]),
+    "ca2_cache_create_staged": (_I32, [ctypes.POINTER(Ca2Config), ctypes.POINTER(_P)]),
+    "ca2_qkv_proj_stage": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
+    "ca2_cache_commit": (_I32, [_P]),
     "ca2_cache_destroy": (None, [_P]),
     "ca2_cache_write": (_I32, [_P, _P, _P, _P, _P, _I32, _P]),
     "ca2_temporal_attn": (_I32, [_P, _P, _P, _P, _P, _I32, ctypes.c_float, _P]),
@@ -170,6 +176,13 @@ def ca2_cache_create(cfg: Ca2Config):
     return h
 
 
+def ca2_cache_create_staged(cfg: Ca2Config):
+    lib = load()
+    h = _P()
+    _check(lib.ca2_cache_create_staged(ctypes.byref(cfg), ctypes.byref(h)), "ca2_cache_create_staged")
+    return h
+
+
 def ca2_cache_destroy(handle):
     load().ca2_cache_destroy(handle)
 
@@ -278,17 +291,20 @@ def ca2_toy_linear(x, w, y, r=None, act=0, stream=None):
 class Cache:
     """Owner of one ca2_cache handle, with shape/dtype checks on its calls."""
 
-    def __init__(self, B, H, d, S, l, p_max, p_spatial, tpe_len, dtype="bf16"):
+    def __init__(self, B, H, d, S, l, p_max, p_spatial, tpe_len, dtype="bf16", staged=False):
+        """staged=True: ca2_cache_create_staged (P_max + l ring slots, for
+        ca2_qkv_proj_stage / ca2_cache_commit)."""
         self.shape = dict(B=B, H=H, d=d, S=S, l=l, p_max=p_max, p_spatial=p_spatial,
                           tpe_len=tpe_len, dtype=dtype)
+        self.ring_slots = p_max + (l if staged else 0)
         self.cfg = make_config(B, H, d, S, l, p_max, p_spatial, tpe_len, dtype)
         self._lib = load()
-        self.handle = ca2_cache_create(self.cfg)
+        self.handle = (ca2_cache_create_staged if staged else ca2_cache_create)(self.cfg)
 
     @classmethod
-    def from_shape(cls, sh: dict):
+    def from_shape(cls, sh: dict, staged=False):
         return cls(sh["B"], sh["H"], sh["d"], sh["S"], sh["l"], sh["p_max"], sh["p_spatial"],
-                   sh["tpe_len"], sh["dtype"])
+                   sh["tpe_len"], sh["dtype"], staged=staged)
 
     def close(self):
         if getattr(self, "handle", None) is not None:
@@ -326,9 +342,12 @@ class Cache:
                                          n, _stream(stream)), "ca2_cache_write")
 
     def ca2_temporal_attn(self, q, k_new, v_new, out, scale=None, stream=None):
+        """k_new = v_new = None: the new frames are the ones staged in the ring."""
         n = q.shape[1]
+        staged = k_new is None and v_new is None
         for nm, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("out", out)):
-            self._chk(nm, t, n)
+            if not (staged and nm in ("k_new", "v_new")):
+                self._chk(nm, t, n)
         scale = self.shape["d"] ** -0.5 if scale is None else scale
         _check(self._lib.ca2_temporal_attn(self.handle, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out),
                                            n, scale, _stream(stream)), "ca2_temporal_attn")
@@ -350,7 +369,8 @@ class Cache:
         info = Ca2CacheInfo()
         _check(self._lib.ca2_cache_info_get(self.handle, ctypes.byref(info)), "ca2_cache_info_get")
         return dict(p_k=info.p_k, head_slot=info.head_slot, spatial_frames=info.spatial_frames,
-                    frames_written=info.frames_written, bytes_resident=info.bytes_resident)
+                    staged_frames=info.staged_frames, frames_written=info.frames_written,
+                    bytes_resident=info.bytes_resident, ring_slots=info.ring_slots)
 
     def ca2_cache_slot_map(self):
         out = (_I32 * self.shape["p_max"])()
@@ -372,7 +392,7 @@ class Cache:
         import numpy as np
         sh = self.shape
         npdt = np.uint16 if sh["dtype"] == "bf16" else np.float32
-        ring = np.empty((sh["B"], sh["p_max"], sh["S"], sh["H"], sh["d"]), dtype=npdt)
+        ring = np.empty((sh["B"], self.ring_slots, sh["S"], sh["H"], sh["d"]), dtype=npdt)
         ringv = np.empty_like(ring)
         sp = np.empty((sh["B"], sh["p_spatial"], sh["S"], sh["H"], sh["d"]), dtype=npdt)
         spv = np.empty_like(sp)
@@ -380,3 +400,33 @@ class Cache:
         _check(self._lib.ca2_cache_debug_copy(self.handle, ptr(ring), ptr(ringv), ptr(sp), ptr(spv),
                                               _stream(stream)), "ca2_cache_debug_copy")
         return ring, ringv, sp, spv
+
+    def ca2_qkv_proj_stage(self, x, w, tpe_rows=None, q=None, k=None, v=None,
+                           targets=CA2_STAGE_RING | CA2_STAGE_SPATIAL, stream=None):
+        """x: [B][n][S][c_in] bf16; w: [3C][c_in] bf16; tpe_rows: [tpe_len][3C]
+        float32 or None; q/k/v: [B][n][S][H][d] bf16 outputs or None."""
+        import torch
+        sh = self.shape
+        if x.dim() != 4 or x.dtype != torch.bfloat16 or not x.is_contiguous() or not x.is_cuda:
+            raise ValueError(f"ca2_qkv_proj_stage: x must be contiguous cuda bf16 [B][n][S][c_in], got "
+                             f"{x.dtype} {tuple(x.shape)}")
+        B, n, S, c_in = x.shape
+        C = sh["H"] * sh["d"]
+        if (B, S) != (sh["B"], sh["S"]):
+            raise ValueError(f"ca2_qkv_proj_stage: x shape {tuple(x.shape)} does not match the cache")
+        if w.dtype != torch.bfloat16 or not w.is_contiguous() or tuple(w.shape) != (3 * C, c_in) or not w.is_cuda:
+            raise ValueError(f"ca2_qkv_proj_stage: w must be contiguous cuda bf16 {(3 * C, c_in)}")
+        if tpe_rows is not None and (tpe_rows.dtype != torch.float32 or not tpe_rows.is_contiguous()
+                                     or tuple(tpe_rows.shape) != (sh["tpe_len"], 3 * C) or not tpe_rows.is_cuda):
+            raise ValueError(f"ca2_qkv_proj_stage: tpe_rows must be contiguous cuda float32 {(sh['tpe_len'], 3 * C)}")
+        for nm, t in (("q", q), ("k", k), ("v", v)):
+            if t is not None:
+                if t.dtype != torch.bfloat16:
+                    raise ValueError(f"ca2_qkv_proj_stage: {nm} must be bf16")
+                self._chk(nm, t, n)
+        _check(self._lib.ca2_qkv_proj_stage(self.handle, _ptr(x), _ptr(w), _ptr(tpe_rows), _ptr(q), _ptr(k),
+                                            _ptr(v), c_in, n, int(targets), _stream(stream)),
+               "ca2_qkv_proj_stage")
+
+    def ca2_cache_commit(self):
+        _check(self._lib.ca2_cache_commit(self.handle), "ca2_cache_commit")

@@ -2,10 +2,13 @@
 // bookkeeping and kernel launches behind the C ABI declared in include/ca2.h.
 //
 // The whole queue state is one counter, frames_written (F_w). Clean frame F
-// lives in ring slot F mod P_max; the queue holds the last
-// P_k = min(F_w, P_max) frames, the oldest in slot (F_w - P_k) mod P_max
+// lives in ring slot F mod R, R the ring's slot count (P_max, or P_max + l for
+// a cache created with staging slots); the queue holds the last
+// P_k = min(F_w, P_max) frames, the oldest in slot (F_w - P_k) mod R
 // (Ca2-VDM notes, key design 4: FIFO queue capped at P_max, oldest leaves
-// first). The spatial buffer keeps the last P' clean frames, frame F in slot
+// first). With R >= P_max + l the next chunk's slots hold no queued frame, so
+// the cache-writing projection can store the chunk's K/V there before the
+// chunk's own attention has read the queue; a commit then advances F_w. The spatial buffer keeps the last P' clean frames, frame F in slot
 // F mod P' (key design 5); while fewer than P' exist, the oldest fills the
 // missing logical positions. TPE index of frame F is F mod L_tpe (key design
 // 4, Cyclic-TPEs).
@@ -26,6 +29,9 @@ struct ca2_cache {
   ca2_config cfg;
   int64_t frames_written;
   int64_t frame_bytes;   // S * H * d * elem: one (batch entry, frame) block
+  int32_t ring_slots;    // R: P_max, or P_max + chunk with staging slots
+  int32_t staged_n;      // frames written by ca2_qkv_proj_stage, not yet committed
+  int32_t staged_targets;
   void* ring_k;
   void* ring_v;
   void* sp_k;
@@ -116,7 +122,14 @@ int32_t queue_len(const ca2_cache* c) {
 }
 
 int32_t queue_head(const ca2_cache* c) {
-  return (int32_t)((c->frames_written - queue_len(c)) % c->cfg.p_max);
+  return (int32_t)((c->frames_written - queue_len(c)) % c->ring_slots);
+}
+
+ca2_status check_not_staged(const ca2_cache* c, const char* what) {
+  if (c->staged_n)
+    return fail(CA2_ERR_STATE, "%s: %d staged frames are not committed (call ca2_cache_commit)", what,
+                c->staged_n);
+  return CA2_OK;
 }
 
 // Logical spatial position j -> absolute frame (oldest first, padded by the
@@ -150,7 +163,11 @@ uint64_t ca2_bytes_resident(const ca2_config* cfg) {
   return 2ull * cfg->batch * (uint64_t)(cfg->p_max + cfg->p_spatial) * frame;
 }
 
-ca2_status ca2_cache_create(const ca2_config* cfg, ca2_cache** out) {
+}  // extern "C"
+
+namespace {
+
+ca2_status create_impl(const ca2_config* cfg, bool staging, ca2_cache** out) {
   if (!out) return fail(CA2_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   ca2_status st = check_config(cfg);
@@ -160,7 +177,10 @@ ca2_status ca2_cache_create(const ca2_config* cfg, ca2_cache** out) {
   c->cfg = *cfg;
   c->frames_written = 0;
   c->frame_bytes = (int64_t)cfg->tokens * cfg->heads * cfg->head_dim * elem_bytes(cfg->dtype);
-  const size_t ring_bytes = (size_t)cfg->batch * cfg->p_max * c->frame_bytes;
+  c->ring_slots = cfg->p_max + (staging ? cfg->chunk : 0);
+  c->staged_n = 0;
+  c->staged_targets = 0;
+  const size_t ring_bytes = (size_t)cfg->batch * c->ring_slots * c->frame_bytes;
   const size_t sp_bytes = (size_t)cfg->batch * cfg->p_spatial * c->frame_bytes;
   // Unwritten slots are filled with 0xFF bytes (a NaN in both dtypes) when
   // CA2_NAN_CANARY=1, so a kernel reading a slot it should not shows up as NaN.
@@ -188,6 +208,14 @@ ca2_status ca2_cache_create(const ca2_config* cfg, ca2_cache** out) {
   return ok();
 }
 
+}  // namespace
+
+extern "C" {
+
+ca2_status ca2_cache_create(const ca2_config* cfg, ca2_cache** out) { return create_impl(cfg, false, out); }
+
+ca2_status ca2_cache_create_staged(const ca2_config* cfg, ca2_cache** out) { return create_impl(cfg, true, out); }
+
 void ca2_cache_destroy(ca2_cache* c) {
   if (!c) return;
   if (c->ring_k) (void)hipFree(c->ring_k);
@@ -201,9 +229,11 @@ ca2_status ca2_cache_write(ca2_cache* c, const void* k_t, const void* v_t, const
                            const void* v_s, int32_t n, void* stream) {
   ca2_status st = check_frames(c, n);
   if (st != CA2_OK) return st;
+  st = check_not_staged(c, "ca2_cache_write");
+  if (st != CA2_OK) return st;
   st = check_ptrs({k_t, v_t});
   if (st != CA2_OK) return st;
-  const int32_t P = c->cfg.p_max, Ps = c->cfg.p_spatial;
+  const int32_t P = c->cfg.p_max, Ps = c->cfg.p_spatial, R = c->ring_slots;
   if (Ps > 0) {
     st = check_ptrs({k_s, v_s});
     if (st != CA2_OK) return st;
@@ -215,16 +245,16 @@ ca2_status ca2_cache_write(ca2_cache* c, const void* k_t, const void* v_t, const
   const int64_t fw = c->frames_written;
   const int64_t fb = c->frame_bytes;
   int nj = 0;
-  // temporal ring: frame fw+i -> slot (fw+i) mod P; only the last P survive
+  // temporal ring: frame fw+i -> slot (fw+i) mod R; only the last P stay queued
   for (int32_t i = (n > P ? n - P : 0); i < n; ++i) {
-    const int64_t slot = (fw + i) % P;
+    const int64_t slot = (fw + i) % R;
     const void* srcs[2] = {k_t, v_t};
     void* dsts[2] = {c->ring_k, c->ring_v};
     for (int t = 0; t < 2; ++t) {
       a.job[nj].src = static_cast<const unsigned char*>(srcs[t]) + i * fb;
       a.job[nj].dst = static_cast<unsigned char*>(dsts[t]) + slot * fb;
       a.job[nj].src_bstride = (int64_t)n * fb;
-      a.job[nj].dst_bstride = (int64_t)P * fb;
+      a.job[nj].dst_bstride = (int64_t)R * fb;
       ++nj;
     }
   }
@@ -252,7 +282,13 @@ ca2_status ca2_temporal_attn(const ca2_cache* c, const void* q, const void* k_ne
                              void* out, int32_t n, float scale, void* stream) {
   ca2_status st = check_frames(c, n);
   if (st != CA2_OK) return st;
-  st = check_ptrs({q, k_new, v_new, out});
+  // new frames already in the ring: staged by ca2_qkv_proj_stage, not committed
+  const bool from_ring = !k_new && !v_new && c->staged_n > 0 && (c->staged_targets & CA2_STAGE_RING);
+  if (!k_new && !v_new && !from_ring)
+    return fail(CA2_ERR_INVALID_ARG, "k_new and v_new are NULL but no frames are staged in the ring");
+  if (from_ring && n != c->staged_n)
+    return fail(CA2_ERR_INVALID_ARG, "n_frames %d differs from the %d staged frames", n, c->staged_n);
+  st = from_ring ? check_ptrs({q, out}) : check_ptrs({q, k_new, v_new, out});
   if (st != CA2_OK) return st;
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(CA2_ERR_INVALID_ARG, "scale must be finite and > 0");
   ca2::TemporalArgs a;
@@ -263,7 +299,8 @@ ca2_status ca2_temporal_attn(const ca2_cache* c, const void* q, const void* k_ne
   a.n = n;
   a.p_k = queue_len(c);
   a.head = queue_head(c);
-  a.p_max = c->cfg.p_max;
+  a.p_max = c->ring_slots;
+  a.ring_keys = from_ring ? a.p_k + n : a.p_k;
   a.causal = 1;
   a.scale_log2e = scale * 1.4426950408889634f;
   hipError_t e = ca2::launch_temporal(c->cfg.dtype, c->cfg.head_dim, a, static_cast<hipStream_t>(stream));
@@ -290,6 +327,8 @@ ca2_status ca2_spatial_attn(const ca2_cache* c, const void* q, const void* k, co
   if (mode == CA2_SPATIAL_PREFIX && Ps > 0) {
     if (c->frames_written < 1)
       return fail(CA2_ERR_STATE, "prefix mode needs at least one clean frame in the cache");
+    if (c->staged_targets & CA2_STAGE_SPATIAL)
+      return fail(CA2_ERR_STATE, "prefix mode while the spatial buffer holds staged, uncommitted frames");
     a.n_prefix = Ps;
     for (int32_t j = 0; j < Ps; ++j) a.prefix_slot[j] = (int32_t)(spatial_frame(c->frames_written, Ps, j) % Ps);
   }
@@ -318,6 +357,7 @@ ca2_status ca2_temporal_attn_frames(const void* q, const void* k, const void* v,
   a.p_k = 0;
   a.head = 0;
   a.p_max = 1;
+  a.ring_keys = 0;
   a.causal = causal;
   a.scale_log2e = scale * 1.4426950408889634f;
   hipError_t e = ca2::launch_temporal(dtype, d, a, static_cast<hipStream_t>(stream));
@@ -366,9 +406,10 @@ ca2_status ca2_cache_info_get(const ca2_cache* c, ca2_cache_info* out) {
   out->head_slot = queue_head(c);
   const int64_t fw = c->frames_written;
   out->spatial_frames = (int32_t)(fw < c->cfg.p_spatial ? fw : c->cfg.p_spatial);
-  out->reserved = 0;
+  out->staged_frames = c->staged_n;
+  out->ring_slots = c->ring_slots;
   out->frames_written = fw;
-  out->bytes_resident = ca2_bytes_resident(&c->cfg);
+  out->bytes_resident = 2ull * c->cfg.batch * (uint64_t)(c->ring_slots + c->cfg.p_spatial) * c->frame_bytes;
   return ok();
 }
 
@@ -394,7 +435,10 @@ ca2_status ca2_spatial_slot_map_raw(int64_t fw, int32_t Ps, int64_t* frames_out,
 
 ca2_status ca2_cache_slot_map(const ca2_cache* c, int32_t* out) {
   if (!c) return fail(CA2_ERR_INVALID_ARG, "cache is NULL");
-  return ca2_ring_slot_map_raw(c->frames_written, c->cfg.p_max, out, nullptr);
+  const int32_t pk = queue_len(c);
+  if (pk > 0 && !out) return fail(CA2_ERR_INVALID_ARG, "host_out is NULL");
+  for (int32_t j = 0; j < pk; ++j) out[j] = (int32_t)((c->frames_written - pk + j) % c->ring_slots);
+  return ok();
 }
 
 ca2_status ca2_cache_frame_ids(const ca2_cache* c, int64_t* t_out, int64_t* s_out, int32_t* s_slots) {
@@ -407,7 +451,7 @@ ca2_status ca2_cache_frame_ids(const ca2_cache* c, int64_t* t_out, int64_t* s_ou
 
 ca2_status ca2_cache_debug_copy(const ca2_cache* c, void* hk, void* hv, void* hks, void* hvs, void* stream) {
   if (!c) return fail(CA2_ERR_INVALID_ARG, "cache is NULL");
-  const size_t ring = (size_t)c->cfg.batch * c->cfg.p_max * c->frame_bytes;
+  const size_t ring = (size_t)c->cfg.batch * c->ring_slots * c->frame_bytes;
   const size_t sp = (size_t)c->cfg.batch * c->cfg.p_spatial * c->frame_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   struct { void* dst; const void* src; size_t n; } cp[4] = {
@@ -429,9 +473,77 @@ ca2_status ca2_qkv_proj(const void* x, const void* w, void* q, void* k, void* v,
   if (m < 1 || c_in < 64 || c_out < 64 || c_in % 64 || c_out % 64)
     return fail(CA2_ERR_INVALID_ARG, "m >= 1, c_in and c_out multiples of 64");
   if ((int64_t)m * c_in > ((int64_t)1 << 40)) return fail(CA2_ERR_INVALID_ARG, "too large");
-  ca2::ProjArgs a{x, w, q, k, v, m, c_in, c_out};
+  ca2::ProjArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x; a.w = w; a.q = q; a.k = k; a.v = v;
+  a.m = m; a.c_in = c_in; a.c_out = c_out;
   hipError_t e = ca2::launch_qkv_proj(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "qkv_proj launch");
+  return ok();
+}
+
+ca2_status ca2_qkv_proj_stage(ca2_cache* c, const void* x, const void* w, const float* tpe_rows, void* q,
+                              void* k, void* v, int32_t c_in, int32_t n, int32_t targets, void* stream) {
+  ca2_status st = check_frames(c, n);
+  if (st != CA2_OK) return st;
+  if (c->cfg.dtype != CA2_BF16) return fail(CA2_ERR_UNSUPPORTED, "the projection is built for bf16 caches only");
+  st = check_ptrs({x, w});
+  if (st != CA2_OK) return st;
+  for (const void* p : {(const void*)tpe_rows, (const void*)q, (const void*)k, (const void*)v})
+    if (p && !aligned16(p)) return fail(CA2_ERR_INVALID_ARG, "tpe_rows / q / k / v must be 16-byte aligned");
+  if (targets < 1 || targets > (CA2_STAGE_RING | CA2_STAGE_SPATIAL))
+    return fail(CA2_ERR_INVALID_ARG, "targets %d: a nonempty combination of CA2_STAGE_RING, CA2_STAGE_SPATIAL",
+                targets);
+  const int32_t c_out = c->cfg.heads * c->cfg.head_dim;
+  if (c_in < 64 || c_in % 64 || c_out % 64)
+    return fail(CA2_ERR_INVALID_ARG, "c_in (%d) and heads * head_dim (%d) must be multiples of 64", c_in, c_out);
+  const int64_t m = (int64_t)c->cfg.batch * n * c->cfg.tokens;
+  if (m > 0x7fffffff || m * c_in > ((int64_t)1 << 40)) return fail(CA2_ERR_INVALID_ARG, "too large");
+  if ((targets & CA2_STAGE_RING) && c->ring_slots < c->cfg.p_max + n)
+    return fail(CA2_ERR_STATE, "ring staging needs a cache created with ca2_cache_create_staged");
+  if (c->staged_n && (c->staged_n != n || (c->staged_targets & targets)))
+    return fail(CA2_ERR_STATE, "already staged: %d frames, targets %d", c->staged_n, c->staged_targets);
+  const int64_t fw = c->frames_written;
+  const int32_t Ps = c->cfg.p_spatial;
+  ca2::ProjArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x; a.w = w; a.q = q; a.k = k; a.v = v;
+  a.m = (int32_t)m; a.c_in = c_in; a.c_out = c_out;
+  a.tpe = tpe_rows;
+  a.tokens = c->cfg.tokens;
+  a.frames = n;
+  a.tpe_len = c->cfg.tpe_len;
+  a.tpe_first = (int32_t)(fw % c->cfg.tpe_len);
+  a.ring_slots = c->ring_slots;
+  a.ring_first = (int32_t)(fw % c->ring_slots);
+  if (targets & CA2_STAGE_RING) {
+    a.ring_k = c->ring_k;
+    a.ring_v = c->ring_v;
+  }
+  if ((targets & CA2_STAGE_SPATIAL) && Ps > 0) {
+    a.sp_k = c->sp_k;
+    a.sp_v = c->sp_v;
+    a.sp_slots = Ps;
+    a.sp_first = (int32_t)(fw % Ps);
+    a.sp_from = n > Ps ? n - Ps : 0;
+  }
+  hipError_t e = ca2::launch_qkv_proj_stage(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "qkv_proj_stage launch");
+  c->staged_n = n;
+  c->staged_targets |= targets;
+  return ok();
+}
+
+ca2_status ca2_cache_commit(ca2_cache* c) {
+  if (!c) return fail(CA2_ERR_INVALID_ARG, "cache is NULL");
+  if (!c->staged_n) return fail(CA2_ERR_STATE, "no staged frames to commit");
+  const int32_t need = CA2_STAGE_RING | (c->cfg.p_spatial > 0 ? CA2_STAGE_SPATIAL : 0);
+  if ((c->staged_targets & need) != need)
+    return fail(CA2_ERR_STATE, "staged targets %d; a commit needs the ring%s", c->staged_targets,
+                c->cfg.p_spatial > 0 ? " and the spatial buffer" : "");
+  c->frames_written += c->staged_n;
+  c->staged_n = 0;
+  c->staged_targets = 0;
   return ok();
 }
 

@@ -23,7 +23,10 @@ struct TemporalArgs {
   int32_t n;               // new frames (queries per row)
   int32_t p_k;             // queued frames
   int32_t head;            // ring slot of the oldest queued frame
-  int32_t p_max;           // ring slots
+  int32_t p_max;           // ring slots (the modulus of the slot arithmetic)
+  int32_t ring_keys;       // keys 0..ring_keys-1 are read from ring slots (head + j) mod p_max:
+                           // p_k, or p_k + n when the new frames were already written
+                           // into the slots after the queue (k_new / v_new unused)
   int32_t causal;          // 1: lower-triangular mask over the new frames; 0: no mask
   float scale_log2e;       // softmax scale * log2(e)
 };
@@ -60,6 +63,13 @@ struct CopyArgs {
   int64_t frame_bytes;
 };
 
+// [Q K V] = X W^T. The plain projection writes q/k/v ([m][c_out]). The
+// cache-writing form (kernel template kStage) takes rows as (b, f, s) of
+// B x frames x tokens, adds the frame's table row to every output (fp32, before
+// rounding), writes any of q/k/v that is not NULL, and also writes the K and
+// V columns straight into the ring (frame f -> slot (ring_first + f) mod
+// ring_slots) and, for frames f >= sp_from, into the spatial buffer
+// (slot (sp_first + f) mod sp_slots). Ring and buffer are [B][slots][tokens][c_out].
 struct ProjArgs {
   const void* x;
   const void* w;
@@ -67,6 +77,15 @@ struct ProjArgs {
   void* k;
   void* v;
   int32_t m, c_in, c_out;
+  const float* tpe;              // [tpe_len][3 * c_out] or NULL
+  void* ring_k;                  // or NULL
+  void* ring_v;
+  void* sp_k;                    // or NULL
+  void* sp_v;
+  int32_t tokens, frames;        // row m = (b * frames + f) * tokens + s
+  int32_t tpe_len, tpe_first;    // row of frame f: (tpe_first + f) mod tpe_len
+  int32_t ring_slots, ring_first;
+  int32_t sp_slots, sp_first, sp_from;
 };
 
 // fp32 linear layer of the toy block: y = act(x w) (+ r), row-major with
@@ -87,6 +106,7 @@ hipError_t launch_temporal(int dtype, int head_dim, const TemporalArgs& a, hipSt
 hipError_t launch_spatial(int dtype, int head_dim, const SpatialArgs& a, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s);
+hipError_t launch_qkv_proj_stage(const ProjArgs& a, hipStream_t s);
 
 hipError_t launch_toy_temb_mod(const float* t, int frames, const float* wmod, int temb_dim, int width, float* out,
                                hipStream_t s);

@@ -21,6 +21,13 @@
 // (one wavefront per SIMD: nothing else would hide the LDS latency).
 // Workgroups are dealt so that each XCD takes a contiguous run of tiles
 // sharing token panels.
+//
+// Cache-writing form (the stage that stores a clean chunk's K/V): the
+// epilogue adds the projected cyclic temporal position embedding row of each
+// token's frame (Ca2-VDM notes, key design 4, Cyclic-TPEs: the embedding is
+// bound into the cached K/V) and writes the K/V columns straight into their
+// ring slots and spatial-buffer slots, so no separate copy of the chunk is
+// needed.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -41,6 +48,7 @@ constexpr int NI = TN * kSlots / 64;    // copy instructions per operand per k-t
 constexpr int kPer = 2 * NI / kWaves;   // per wavefront per k-tile (9)
 static_assert(TN == TM && (TN * kSlots) % 64 == 0 && (2 * NI) % kWaves == 0, "copy geometry");
 
+template <bool kStage>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void qkv_proj_kernel(ProjArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * STAGE];
   const int tid = threadIdx.x;
@@ -127,34 +135,102 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // register r of acc[i][j]: channel n0 + wn*128 + 32i + 8(r/4) + 4*half + r%4,
   // token m0 + wm*64 + 32j + col
+  if constexpr (!kStage) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int m = m0 + wm * 64 + 32 * j + col;
-    if (m >= a.m) continue;
+    for (int j = 0; j < 2; ++j) {
+      const int m = m0 + wm * 64 + 32 * j + col;
+      if (m >= a.m) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 128 + 32 * i + 8 * g + 4 * half;
-        if (n >= N) continue;
-        const int seg = n / a.c_out;
-        bf16_t* dst = static_cast<bf16_t*>(seg == 0 ? a.q : seg == 1 ? a.k : a.v);
-        uint2 v;
-        v.x = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-        v.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-        *reinterpret_cast<uint2*>(dst + (int64_t)m * a.c_out + (n - seg * a.c_out)) = v;
-      }
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * 128 + 32 * i + 8 * g + 4 * half;
+          if (n >= N) continue;
+          const int seg = n / a.c_out;
+          bf16_t* dst = static_cast<bf16_t*>(seg == 0 ? a.q : seg == 1 ? a.k : a.v);
+          uint2 v;
+          v.x = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+          v.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          *reinterpret_cast<uint2*>(dst + (int64_t)m * a.c_out + (n - seg * a.c_out)) = v;
+        }
+    }
+  } else {
+    // cache-writing epilogue: + the frame's table row, then the caller's
+    // outputs and the cache slots of the K and V columns. A run of 4
+    // channels never crosses a Q/K/V boundary (c_out is a multiple of 64).
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = m0 + wm * 64 + 32 * j + col;
+      if (m >= a.m) continue;
+      const int bf = m / a.tokens;                 // b * frames + f
+      const int s_tok = m - bf * a.tokens;
+      const int b = bf / a.frames;
+      const int f = bf - b * a.frames;
+      const float* trow = a.tpe ? a.tpe + (int64_t)((a.tpe_first + f) % a.tpe_len) * N : nullptr;
+      const int64_t ring_row =
+          ((int64_t)b * a.ring_slots + (a.ring_first + f) % a.ring_slots) * a.tokens + s_tok;
+      const bool to_sp = a.sp_k != nullptr && f >= a.sp_from;
+      const int64_t sp_row = to_sp ? ((int64_t)b * a.sp_slots + (a.sp_first + f) % a.sp_slots) * a.tokens + s_tok : 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * 128 + 32 * i + 8 * g + 4 * half;
+          if (n >= N) continue;
+          float o0 = acc[i][j][4 * g + 0], o1 = acc[i][j][4 * g + 1];
+          float o2 = acc[i][j][4 * g + 2], o3 = acc[i][j][4 * g + 3];
+          if (trow) {
+            const float4 t = *reinterpret_cast<const float4*>(trow + n);
+            o0 += t.x; o1 += t.y; o2 += t.z; o3 += t.w;
+          }
+          uint2 v;
+          v.x = pack_bf16x2(o0, o1);
+          v.y = pack_bf16x2(o2, o3);
+          const int seg = n / a.c_out;
+          const int c = n - seg * a.c_out;
+          void* own = seg == 0 ? a.q : seg == 1 ? a.k : a.v;
+          if (own) *reinterpret_cast<uint2*>(static_cast<bf16_t*>(own) + (int64_t)m * a.c_out + c) = v;
+          if (seg == 0) continue;
+          void* rd = seg == 1 ? a.ring_k : a.ring_v;
+          if (rd) *reinterpret_cast<uint2*>(static_cast<bf16_t*>(rd) + ring_row * a.c_out + c) = v;
+          if (to_sp)
+            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(seg == 1 ? a.sp_k : a.sp_v) + sp_row * a.c_out + c) = v;
+        }
+    }
   }
 }
 
 }  // namespace
 
+namespace {
+bool proj_geometry(const ProjArgs& a, int64_t& tiles) {
+  if (a.m < 1 || a.c_in < TK || a.c_in % TK || a.c_out < 64 || a.c_out % 64) return false;
+  if ((int64_t)TN * a.c_in * 2 > 0xffffffffLL) return false;   // 32-bit copy offsets
+  tiles = (int64_t)((3 * a.c_out + TN - 1) / TN) * ((a.m + TM - 1) / TM);
+  return tiles <= 0x7fffffff;
+}
+}  // namespace
+
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s) {
-  if (a.m < 1 || a.c_in % TK || a.c_out % 64) return hipErrorInvalidValue;
-  if ((int64_t)TN * a.c_in * 2 > 0xffffffffLL) return hipErrorInvalidValue;   // 32-bit copy offsets
-  const int64_t tiles = (int64_t)((3 * a.c_out + TN - 1) / TN) * ((a.m + TM - 1) / TM);
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(qkv_proj_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+  int64_t tiles;
+  if (!proj_geometry(a, tiles)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(qkv_proj_kernel<false>, dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_proj_stage(const ProjArgs& a, hipStream_t s) {
+  int64_t tiles;
+  if (!proj_geometry(a, tiles)) return hipErrorInvalidValue;
+  // rows are whole (b, frame) blocks; every modulus is positive and every
+  // first index already reduced
+  if (a.tokens < 1 || a.frames < 1 || a.m % ((int64_t)a.tokens * a.frames)) return hipErrorInvalidValue;
+  if (a.tpe && (a.tpe_len < 1 || a.tpe_first < 0 || a.tpe_first >= a.tpe_len)) return hipErrorInvalidValue;
+  if ((a.ring_k != nullptr) != (a.ring_v != nullptr) || (a.sp_k != nullptr) != (a.sp_v != nullptr))
+    return hipErrorInvalidValue;
+  if (a.ring_slots < 1 || a.ring_first < 0 || a.ring_first >= a.ring_slots) return hipErrorInvalidValue;
+  if (a.sp_k && (a.sp_slots < 1 || a.sp_first < 0 || a.sp_first >= a.sp_slots || a.sp_from < 0))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(qkv_proj_kernel<true>, dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(64 * kWaves) void temporal_attn_kernel(TemporalArgs
         const T* kb;
         const T* vb;
         int64_t base;
-        if (j < a.p_k) {
+        if (j < a.ring_keys) {
           int slot = a.head + j;
           if (slot >= a.p_max) slot -= a.p_max;
           base = ((int64_t)ch_b[c] * a.p_max + slot) * frame_elems;
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
   const int ke = min(k_lim, kb + per);
 
   auto key_row = [&](int j, const unsigned char* ring, const unsigned char* fresh) -> const unsigned char* {
-    if (j < a.p_k) {
+    if (j < a.ring_keys) {
       int slot = a.head + j;
       if (slot >= a.p_max) slot -= a.p_max;
       return ring + ((int64_t)b * a.p_max + slot) * frame_bytes + row_bytes;
@@ -551,6 +551,10 @@ bool temporal_supported(int dtype, int d) {
 
 hipError_t launch_temporal(int dtype, int d, const TemporalArgs& a, hipStream_t s) {
   if (a.n < 1 || a.p_k < 0) return hipErrorInvalidValue;
+  // ring keys: the queue, or the queue and the new frames; slot = head + j
+  // needs at most one wrap
+  if (a.ring_keys != a.p_k && a.ring_keys != a.p_k + a.n) return hipErrorInvalidValue;
+  if (a.ring_keys > 0 && (a.head < 0 || a.head >= a.p_max || a.ring_keys > a.p_max)) return hipErrorInvalidValue;
   if (dtype == 0) {
     switch (d) {
       case 16: return launch_td<float, 16>(a, s);

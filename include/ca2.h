@@ -16,6 +16,10 @@
  * one chunk's spatial K/V, overwritten every autoregressive step). The cache is
  * read by every denoising call and written only by ca2_cache_write, so one
  * copy serves all T denoising steps ([notes] key design 2, cache sharing).
+ * A cache created with staging slots (ca2_cache_create_staged) can instead
+ * receive a clean chunk's K/V straight from the cache-writing projection
+ * (ca2_qkv_proj_stage, which also binds the cyclic TPE row into them) and
+ * take it into the queue with ca2_cache_commit, with no separate copy.
  * Beside the cache object: the QKV projection of the cache-writing pass,
  * cache-less attention over T frames (the recompute baseline the cache
  * removes), and the pieces of a small random-weight block used to check the
@@ -24,7 +28,8 @@
  * Conventions (all entry points):
  *   - Layout of every activation tensor: [B][n][S][H][d] contiguous
  *     (batch, frame, spatial token, head, head dim); the ring is
- *     [B][P_max][S][H][d] and the spatial buffer [B][P'][S][H][d].
+ *     [B][R][S][H][d] with R = P_max ring slots (P_max + chunk for a cache
+ *     with staging slots) and the spatial buffer [B][P'][S][H][d].
  *   - Device pointers are owned by the caller, must be 16-byte aligned and
  *     must not alias the output. The library never frees them.
  *   - `stream` is a hipStream_t passed as void* (NULL = legacy default stream).
@@ -78,13 +83,21 @@ typedef struct {
   int32_t dtype;       /* ca2_dtype */
 } ca2_config;
 
+/* Where ca2_qkv_proj_stage writes a chunk's K/V (bit flags). */
+typedef enum {
+  CA2_STAGE_RING = 1,        /* the temporal ring's slots after the queue */
+  CA2_STAGE_SPATIAL = 2      /* the spatial buffer (the chunk's last P' frames) */
+} ca2_stage_target;
+
 typedef struct {
   int32_t p_k;              /* frames in the temporal queue, min(frames_written, p_max) */
   int32_t head_slot;        /* ring slot of the oldest queued frame */
   int32_t spatial_frames;   /* distinct clean frames held by the spatial buffer */
-  int32_t reserved;
-  int64_t frames_written;   /* clean frames ever written */
+  int32_t staged_frames;    /* frames staged by ca2_qkv_proj_stage, not yet committed */
+  int64_t frames_written;   /* clean frames ever written (committed) */
   uint64_t bytes_resident;  /* device bytes of ring + spatial buffer */
+  int32_t ring_slots;       /* R: physical ring slots (p_max, or p_max + chunk) */
+  int32_t reserved;
 } ca2_cache_info;
 
 /*
@@ -97,6 +110,17 @@ typedef struct {
  * not built), OUT_OF_MEMORY, HIP. On error *out is set to NULL.
  */
 ca2_status ca2_cache_create(const ca2_config* cfg, ca2_cache** out);
+
+/*
+ * Same, with a ring of R = P_max + chunk slots (2 * B*(P_max+chunk)*S*H*d
+ * elements). Frame F lives in slot F mod R, so the slots of the next chunk
+ * never hold a queued frame: the chunk's K/V can be written there by
+ * ca2_qkv_proj_stage while the queue still holds the frames the chunk's own
+ * attention must see ([notes] overall framework: the cache-writing pass
+ * attends with the context it was denoised with; eviction comes after).
+ * Every other entry point works on such a cache as on a plain one.
+ */
+ca2_status ca2_cache_create_staged(const ca2_config* cfg, ca2_cache** out);
 
 /* Free the cache's device buffers and the object. NULL-safe. The caller must
  * make sure no enqueued work still uses the cache. */
@@ -115,6 +139,7 @@ void ca2_cache_destroy(ca2_cache* cache);
  * clean frames in the spatial buffer (frame F at slot F mod P'). Copies are
  * bitwise. 1 <= n_frames <= chunk. Enqueue this after the cache-writing
  * pass's attention calls: they must see the queue before eviction.
+ * STATE while frames staged by ca2_qkv_proj_stage are not committed.
  */
 ca2_status ca2_cache_write(ca2_cache* cache, const void* k_t, const void* v_t,
                            const void* k_s, const void* v_s, int32_t n_frames,
@@ -128,6 +153,9 @@ ca2_status ca2_cache_write(ca2_cache* cache, const void* k_t, const void* v_t,
  * softmax(scale * q_i . K^T) V over exactly those P_k + i + 1 keys.
  * q, k_new, v_new, out: [B][n][S][H][d] in the cache's dtype.
  * 1 <= n_frames <= chunk; scale > 0 and finite (normally 1/sqrt(d)).
+ * k_new and v_new may both be NULL when n_frames frames are staged in the
+ * ring by ca2_qkv_proj_stage: the new keys/values are then read from their
+ * ring slots (the cache-writing pass's attention before the commit).
  * Reads the cache, never writes it.
  */
 ca2_status ca2_temporal_attn(const ca2_cache* cache, const void* q, const void* k_new,
@@ -140,6 +168,7 @@ ca2_status ca2_temporal_attn(const ca2_cache* cache, const void* q, const void* 
  *   the S tokens of each of the P' spatial-buffer frames (oldest first), a
  *   map of S x (P'+1)S. While fewer than P' clean frames exist the oldest one
  *   fills the missing positions. Needs frames_written >= 1 (else STATE).
+ *   STATE while staged frames in the spatial buffer are not committed.
  * CA2_SPATIAL_SELF: keys/values are the frame's own S tokens (the clean-frame
  *   self-repeat case, whose value equals plain self-attention).
  * q, k, v, out: [B][n][S][H][d]. 1 <= n_frames <= chunk.
@@ -189,7 +218,8 @@ ca2_status ca2_tpe_index_raw(int64_t first_frame, int32_t n, int32_t tpe_len,
 /* Snapshot of the host-side state. */
 ca2_status ca2_cache_info_get(const ca2_cache* cache, ca2_cache_info* out);
 
-/* Ring slot of each logical queue position, oldest first: host_out[p_k]. */
+/* Ring slot of each logical queue position, oldest first: host_out[p_k]
+ * (slot = (frames_written - p_k + j) mod R). */
 ca2_status ca2_cache_slot_map(const ca2_cache* cache, int32_t* host_out);
 
 /* Absolute frame ids held: temporal_out[p_k] oldest first (may be NULL);
@@ -211,12 +241,13 @@ ca2_status ca2_spatial_slot_map_raw(int64_t frames_written, int32_t p_spatial,
 
 /* Bytes the cache for `cfg` holds on the device: 2 * B * (P_max + P') * S *
  * H * d * elem ([notes] GPU-memory table: independent of T). 0 if cfg is
- * invalid. Pure host function. */
+ * invalid. Pure host function. A cache with staging slots holds chunk more
+ * ring frames (ca2_cache_info_get reports the actual bytes). */
 uint64_t ca2_bytes_resident(const ca2_config* cfg);
 
 /* Synchronous copy of the whole ring and spatial buffer to host memory
  * (physical slot order). Any of the pointers may be NULL. Sizes:
- * host_k/host_v B*P_max*S*H*d elements, host_ks/host_vs B*P'*S*H*d. */
+ * host_k/host_v B*R*S*H*d elements, host_ks/host_vs B*P'*S*H*d. */
 ca2_status ca2_cache_debug_copy(const ca2_cache* cache, void* host_k, void* host_v,
                                 void* host_ks, void* host_vs, void* stream);
 
@@ -230,6 +261,47 @@ ca2_status ca2_cache_debug_copy(const ca2_cache* cache, void* host_k, void* host
  */
 ca2_status ca2_qkv_proj(const void* x, const void* w, void* q, void* k, void* v,
                         int32_t m, int32_t c_in, int32_t c_out, void* stream);
+
+/*
+ * The cache-writing projection with the cache write fused into it
+ * ([notes] overall framework, cache-writing stage; key design 4, Cyclic-TPEs:
+ * the temporal position embedding is bound into the cached K/V and keeps the
+ * cyclic index the frame was computed with). For the n clean frames that
+ * follow the committed ones (frames F_w .. F_w+n-1):
+ *   Y = x w^T + tpe_rows[(F_w + f) mod tpe_len]   (row of each token's frame f)
+ * accumulated in float32 and rounded once to bf16; columns [0,C) are Q,
+ * [C,2C) K, [2C,3C) V with C = heads * head_dim.
+ * x: [B][n][S][c_in] bf16; w: [3C][c_in] bf16 (row-major linear weight);
+ * tpe_rows: [tpe_len][3C] float32 table of projected embedding rows (the
+ *   embedding e_i added to the tokens before the projection contributes
+ *   e_i w^T), or NULL for none;
+ * q, k, v: [B][n][S][H][d] bf16 outputs, each may be NULL (not written).
+ * targets (ca2_stage_target flags): CA2_STAGE_RING writes K/V into ring
+ *   slots (F_w + f) mod R -- needs a cache from ca2_cache_create_staged;
+ *   CA2_STAGE_SPATIAL writes the K/V of the last P' frames into the spatial
+ *   buffer (frame F at slot F mod P'). The two may come from two calls (two
+ *   layers' projections) for the same n.
+ * The frames stay staged: the queue and the frame count do not move until
+ * ca2_cache_commit, so the chunk's temporal attention still sees the queue
+ * before eviction (pass k_new = v_new = NULL to read the new frames from the
+ * ring). Bf16 caches only; c_in and C multiples of 64.
+ * Errors: INVALID_ARG (NULL x/w, misaligned pointer, bad sizes or targets),
+ * STATE (ring target without staging slots; a target already staged, or a
+ * different n, since the last commit), UNSUPPORTED (fp32 cache), HIP.
+ */
+ca2_status ca2_qkv_proj_stage(ca2_cache* cache, const void* x, const void* w,
+                              const float* tpe_rows, void* q, void* k, void* v,
+                              int32_t c_in, int32_t n_frames, int32_t targets,
+                              void* stream);
+
+/*
+ * Take the staged frames into the queue: frames_written += n, which appends
+ * them and evicts past P_max exactly as ca2_cache_write does ([notes] key
+ * design 4), and makes the spatial buffer's new frames the prefix. Host state
+ * only (no launch). Needs the ring staged, and the spatial buffer too when
+ * P' > 0; STATE otherwise.
+ */
+ca2_status ca2_cache_commit(ca2_cache* cache);
 
 /*
  * Pieces of a small spatial-temporal transformer block (random weights) for

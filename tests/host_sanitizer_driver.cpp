@@ -102,12 +102,24 @@ int main() {
   if (st == CA2_OK) {
     ca2_cache_info info;
     CHECK(ca2_cache_info_get(h, &info) == CA2_OK && info.p_k == 0 && info.frames_written == 0);
+    CHECK(info.ring_slots == c.p_max && info.staged_frames == 0);
     CHECK(ca2_cache_write(h, nullptr, nullptr, nullptr, nullptr, 1, nullptr) == CA2_ERR_INVALID_ARG);
+    CHECK(ca2_cache_commit(h) == CA2_ERR_STATE);   // nothing staged
+    ca2_cache_destroy(h);
+  } else {
+    CHECK(h == nullptr);
+  }
+  const ca2_status st2 = ca2_cache_create_staged(&c, &h);
+  CHECK(st2 == CA2_OK || st2 == CA2_ERR_HIP || st2 == CA2_ERR_OUT_OF_MEMORY);
+  if (st2 == CA2_OK) {
+    ca2_cache_info info;
+    CHECK(ca2_cache_info_get(h, &info) == CA2_OK && info.ring_slots == c.p_max + c.chunk);
     ca2_cache_destroy(h);
   } else {
     CHECK(h == nullptr);
   }
   ca2_cache_destroy(nullptr);
+  CHECK(ca2_cache_create_staged(nullptr, &h) == CA2_ERR_INVALID_ARG && h == nullptr);
 
   // calls on a NULL cache
   int32_t tpe[4];
@@ -118,6 +130,9 @@ int main() {
   ca2_cache_info info;
   CHECK(ca2_cache_info_get(nullptr, &info) == CA2_ERR_INVALID_ARG);
   CHECK(ca2_cache_slot_map(nullptr, tpe) == CA2_ERR_INVALID_ARG);
+  CHECK(ca2_cache_commit(nullptr) == CA2_ERR_INVALID_ARG);
+  CHECK(ca2_qkv_proj_stage(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 64, 1, 3, nullptr) ==
+        CA2_ERR_INVALID_ARG);
 
   // cache-less and toy entry points: validation before any launch
   void* p = reinterpret_cast<void*>(4096);

@@ -89,9 +89,10 @@ def test_create_rejects_bad_config_before_any_device_call(lib, field, value):
     cfg = lib.make_config(sh["B"], sh["H"], sh["d"], sh["S"], sh["l"], sh["p_max"],
                           sh["p_spatial"], sh["tpe_len"], sh["dtype"])
     setattr(cfg, field, value)
-    with pytest.raises(lib.Ca2Error) as e:
-        lib.ca2_cache_create(cfg)
-    assert e.value.status == lib.CA2_ERR_INVALID_ARG
+    for create in (lib.ca2_cache_create, lib.ca2_cache_create_staged):
+        with pytest.raises(lib.Ca2Error) as e:
+            create(cfg)
+        assert e.value.status == lib.CA2_ERR_INVALID_ARG
     assert lib.ca2_bytes_resident(cfg) == 0
 
 
@@ -109,6 +110,10 @@ def test_null_and_range_errors(lib):
     assert raw.ca2_tpe_index_raw(-1, 2, 13, None) == lib.CA2_ERR_INVALID_ARG
     assert raw.ca2_tpe_index_raw(0, 2, 0, None) == lib.CA2_ERR_INVALID_ARG
     assert raw.ca2_qkv_proj(None, None, None, None, None, 8, 64, 64, None) == lib.CA2_ERR_INVALID_ARG
+    assert raw.ca2_cache_create_staged(None, None) == lib.CA2_ERR_INVALID_ARG
+    assert raw.ca2_qkv_proj_stage(None, None, None, None, None, None, None, 64, 1, 3, None) == \
+        lib.CA2_ERR_INVALID_ARG
+    assert raw.ca2_cache_commit(None) == lib.CA2_ERR_INVALID_ARG
     raw.ca2_cache_destroy(None)   # NULL-safe
     for s in range(6):
         assert lib.ca2_status_string(s)
