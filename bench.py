@@ -477,8 +477,8 @@ def kernel_mode(kernel, workload, reps):
     from causal_kv_cache_amd import ca2
     sh = WORKLOADS[workload]
     if kernel in ("qkv_proj", "qkv_proj_stage"):
-        r = write_case(reps, rounds=1, only=kernel)
-        return {"kernel": kernel, "workload": workload, **r[kernel]}
+        r = write_case(reps, rounds=1, only=kernel)[kernel]
+        return {"kernel": kernel, "workload": workload, "reps": reps, "avg_us": r["us"], "flops": r["flops"]}
     # the same buffers and rotation as the benchmark's per-kernel table
     w = main_workload() if sh is AR_STEP else Workload(sh, 2, seed=99)
     if kernel == "cache_write":
