@@ -172,12 +172,16 @@ ca2_status create_impl(const ca2_config* cfg, bool staging, ca2_cache** out) {
   *out = nullptr;
   ca2_status st = check_config(cfg);
   if (st != CA2_OK) return st;
+  const int64_t slots = (int64_t)cfg->p_max + (staging ? cfg->chunk : 0);
+  const int64_t frame = (int64_t)cfg->tokens * cfg->heads * cfg->head_dim * elem_bytes(cfg->dtype);
+  if (slots > 0x7fffffff || (int64_t)cfg->batch * (slots + cfg->p_spatial) * frame > ((int64_t)1 << 46))
+    return fail(CA2_ERR_INVALID_ARG, "cache too large");
   ca2_cache* c = new (std::nothrow) ca2_cache();
   if (!c) return fail(CA2_ERR_OUT_OF_MEMORY, "host allocation failed");
   c->cfg = *cfg;
   c->frames_written = 0;
-  c->frame_bytes = (int64_t)cfg->tokens * cfg->heads * cfg->head_dim * elem_bytes(cfg->dtype);
-  c->ring_slots = cfg->p_max + (staging ? cfg->chunk : 0);
+  c->frame_bytes = frame;
+  c->ring_slots = (int32_t)slots;
   c->staged_n = 0;
   c->staged_targets = 0;
   const size_t ring_bytes = (size_t)cfg->batch * c->ring_slots * c->frame_bytes;
