@@ -522,6 +522,46 @@ def cpu_baseline(budget_s: float):
             "seconds": el}
 
 
+def cpu_per_kernel():
+    """The oracle's temporal and prefix-spatial attention, as they stand
+    (float64 numpy), timed per call on the host cores: whole calls at the
+    256-token shape; at the batched 32x32-latent shape a stated sample of each
+    call scaled to a whole call (rows, and (batch, frame, head) pairs, are
+    independent, so the work scales linearly). Inputs are drawn before timing."""
+    import numpy as np
+    from oracle import temporal_attn_ref, spatial_attn_ref
+    rng = np.random.default_rng(3)
+
+    def draw(*shape):
+        return rng.standard_normal(shape, dtype=np.float32)
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    res = {}
+    for sh, tb, sample in ((AR_STEP, AR_STEP["B"], None), (LARGE, 1, "spatial: 1 of 1024 (batch, frame, head)")):
+        l, S, H, d, P, Ps = sh["l"], sh["S"], sh["H"], sh["d"], sh["p_max"], sh["p_spatial"]
+        q, k, v = (draw(tb, l, S, H, d) for _ in range(3))
+        rk, rv = draw(tb, P, S, H, d), draw(tb, P, S, H, d)
+        t_t = timed(lambda: temporal_attn_ref(q, k, v, rk, rv, list(range(P)), d ** -0.5)) * sh["B"] / tb
+        del rk, rv
+        if sample:
+            qs, ks_, vs_ = (x[:1, :1, :, :1] for x in (q, k, v))
+            pk, pv = draw(1, Ps, S, 1, d), draw(1, Ps, S, 1, d)
+            scale_up = sh["B"] * l * H
+        else:
+            qs, ks_, vs_ = q, k, v
+            pk, pv = draw(sh["B"], Ps, S, H, d), draw(sh["B"], Ps, S, H, d)
+            scale_up = 1
+        t_s = timed(lambda: spatial_attn_ref(qs, ks_, vs_, pk, pv, list(range(Ps)), d ** -0.5, "prefix")) * scale_up
+        res[sh["name"]] = {"temporal_s_per_call": round(t_t, 4), "spatial_prefix_s_per_call": round(t_s, 4),
+                           "sample": ("whole calls" if not sample else
+                                      f"temporal: batch entry 1 of {sh['B']}; {sample}; scaled to a whole call")}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -617,6 +657,13 @@ def main():
         cb = cpu_baseline(args.cpu_seconds)
         cb.pop("seconds", None)
         cb["value"] = round(cb["value"], 2)
+        per = cpu_per_kernel()
+        gpu = {AR_STEP["name"]: result.get("kernels", {}), LARGE["name"]: result.get("large", {}).get("kernels", {})}
+        for wl, r in per.items():
+            for name, key in (("temporal_attn", "gpu_temporal_us"), ("spatial_attn_prefix", "gpu_spatial_prefix_us")):
+                if name in gpu.get(wl, {}):
+                    r[key] = round(gpu[wl][name]["us"], 3)
+        cb["per_kernel"] = per
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
