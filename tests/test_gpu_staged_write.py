@@ -285,3 +285,49 @@ def test_write_case_full_size_sampled(ca2):
     assert info["p_k"] == P and info["frames_written"] == P + l
     assert info["bytes_resident"] == 2 * B * (P + l + Ps) * S * C * 2
     cache.close()
+
+
+@pytest.mark.parametrize("sh", [
+    dict(B=1, H=1, d=128, S=70, l=3, p_max=4, p_spatial=0, tpe_len=7, dtype="bf16"),     # no spatial buffer
+    dict(B=3, H=8, d=72, S=33, l=8, p_max=9, p_spatial=5, tpe_len=20, dtype="bf16"),     # C = 576, ragged tokens
+], ids=["d128_no_prefix", "d72_ragged"])
+def test_staged_other_shapes(ca2, sh):
+    """Stage + write-pass temporal attention read from the ring + commit over
+    writes that evict and wrap, against the oracle (projection with TPE,
+    attention over the oracle's bf16 K/V); queue placement bit-exact."""
+    B, S, H, d, l, P, Ps = sh["B"], sh["S"], sh["H"], sh["d"], sh["l"], sh["p_max"], sh["p_spatial"]
+    c_in = 64
+    cache = ca2.Cache.from_shape(sh, staged=True)
+    w, rows = _weights(sh, c_in, 36)
+    dw, drows = to_dev(w, "bf16"), torch.from_numpy(rows.astype(np.float32)).cuda()
+    oq = TemporalQueue(P, slots=P + l)
+    ok_frames, ov_frames = {}, {}
+    fw = 0
+    for step, n in enumerate([1, l, 2, l, l]):
+        x = _inputs(sh, c_in, 12, n, step)
+        exact = [_split(t, sh, n) for t in qkv_proj_tpe_ref(x, w, rows, fw, n, S)]
+        q_ref, k_ref, v_ref = (_bf16(t) for t in exact)
+        dq = torch.empty((B, n, S, H, d), dtype=torch.bfloat16, device="cuda")
+        targets = RING | (SPATIAL if Ps else 0)
+        cache.ca2_qkv_proj_stage(to_dev(x, "bf16").view(B, n, S, c_in), dw, drows, dq, None, None, targets=targets)
+        out = torch.empty_like(dq)
+        cache.ca2_temporal_attn(dq, None, None, out)
+        torch.cuda.synchronize()
+        check_close(to_host(dq), exact[0], "bf16", f"step {step} projected q")
+        ids = oq.frame_ids()
+        rk = np.stack([ok_frames[f] for f in ids], 1) if ids else np.zeros((B, 0, S, H, d))
+        rv = np.stack([ov_frames[f] for f in ids], 1) if ids else np.zeros((B, 0, S, H, d))
+        check_close(to_host(out), temporal_attn_ref(q_ref, k_ref, v_ref, rk, rv, list(range(len(ids))), d ** -0.5),
+                    "bf16", f"step {step} write-pass temporal attention")
+        hk, hv, _, _ = cache.ca2_cache_debug_copy()
+        for f in range(n):
+            slot = (fw + f) % (P + l)
+            check_close(bits_to_f32(hk[:, slot]), exact[1][:, f], "bf16", f"ring K frame {fw + f}")
+            check_close(bits_to_f32(hv[:, slot]), exact[2][:, f], "bf16", f"ring V frame {fw + f}")
+        cache.ca2_cache_commit()
+        oq.write(range(fw, fw + n))
+        for f in range(n):
+            ok_frames[fw + f], ov_frames[fw + f] = k_ref[:, f], v_ref[:, f]
+        fw += n
+        assert cache.ca2_cache_slot_map() == oq.slot_map()
+    cache.close()
