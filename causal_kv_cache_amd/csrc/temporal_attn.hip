@@ -392,35 +392,47 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
     for (int e = 0; e < DPL; ++e) acc[qq][e] = 0.f;
   }
 
-  // K/V slices of keys j .. j+3 in a 4-slot register ring: key j+3 is loaded
-  // while key j is processed, so three keys per lane are always in flight.
+  // K/V slices of keys j .. j+3 in a 4-slot register ring, consumed in pairs:
+  // while the pair (j, j+1) is processed the pair (j+2, j+3) is in flight,
+  // and the slots of (j, j+1) are refilled with (j+4, j+5) right after.
   constexpr int kPF = 4;
   Slice<D> kr[kPF], vr[kPF];
 #pragma unroll
-  for (int u = 0; u < kPF - 1; ++u)
+  for (int u = 0; u < kPF; ++u)
     if (row_ok && kb + u < ke) {
       load_slice<D>(kr[u], key_row(kb + u, rkb, knb), g);
       load_slice<D>(vr[u], key_row(kb + u, rvb, vnb), g);
     }
-  auto process = [&](int j, const Slice<D>& kc, const Slice<D>& vc) {
-    // scores of the lane's queries against key j
-    float x[kQPL];
+  // One key pair: scores, lazy rescale, then P of the pair rounded to bf16 and
+  // O += P V as bf16 dot products over the two keys (one v_dot2 per dimension
+  // and query; the row sum is the same dot product with (1, 1), so numerator
+  // and normaliser use the same rounded P). `two` (wavefront-uniform) is false
+  // when key j+1 is past the range: its score is -inf and its V words are
+  // zeroed, so a stale slot cannot turn 0 * V into NaN.
+  auto process2 = [&](int j, const Slice<D>& k0, const Slice<D>& v0, const Slice<D>& k1, const Slice<D>& v1,
+                      bool two) {
+    float x0[kQPL], x1[kQPL];
     bool raise = false;
 #pragma unroll
     for (int qq = 0; qq < kQPL; ++qq) {
-      float s = 0.f;
+      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int w = 0; w < DW; ++w)
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, qs[qq].w[w]),
-                                            __builtin_bit_cast(bf16x2v, kc.w[w]), s, false);
-      s = quad_sum(s);
-      x[qq] = (j <= last_key[qq]) ? s * a.scale_log2e : -INFINITY;
-      raise |= x[qq] > m[qq] + kLazy;
+      for (int w = 0; w < DW; ++w) {
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, qs[qq].w[w]),
+                                             __builtin_bit_cast(bf16x2v, k0.w[w]), s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, qs[qq].w[w]),
+                                             __builtin_bit_cast(bf16x2v, k1.w[w]), s1, false);
+      }
+      s0 = quad_sum(s0);
+      s1 = quad_sum(s1);
+      x0[qq] = (j <= last_key[qq]) ? s0 * a.scale_log2e : -INFINITY;
+      x1[qq] = (two && j + 1 <= last_key[qq]) ? s1 * a.scale_log2e : -INFINITY;
+      raise |= fmaxf(x0[qq], x1[qq]) > m[qq] + kLazy;
     }
     if (raise) {
 #pragma unroll
       for (int qq = 0; qq < kQPL; ++qq) {
-        const float mn = fmaxf(m[qq], x[qq]);
+        const float mn = fmaxf(m[qq], fmaxf(x0[qq], x1[qq]));
         const float corr = fast_exp2(m[qq] - mn);
         m[qq] = mn;
         l[qq] *= corr;
@@ -428,31 +440,37 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
         for (int e = 0; e < DPL; ++e) acc[qq][e] *= corr;
       }
     }
-    float v[DPL];
+    // V of the pair by dimension: word 2w+h holds (v0, v1) of dimension 2w+h
+    uint32_t vp[DPL];
 #pragma unroll
     for (int w = 0; w < DW; ++w) {
-      v[2 * w] = bf16_lo(vc.w[w]);
-      v[2 * w + 1] = bf16_hi(vc.w[w]);
+      const uint32_t b = two ? v1.w[w] : 0u;
+      vp[2 * w] = __builtin_amdgcn_perm(b, v0.w[w], 0x05040100u);       // low halves
+      vp[2 * w + 1] = __builtin_amdgcn_perm(b, v0.w[w], 0x07060302u);   // high halves
     }
 #pragma unroll
     for (int qq = 0; qq < kQPL; ++qq) {
-      const float p = fast_exp2(x[qq] - m[qq]);   // 0 for hidden keys
-      l[qq] += p;
+      const bf16x2v pp = __builtin_bit_cast(bf16x2v, pack_bf16x2(fast_exp2(x0[qq] - m[qq]), fast_exp2(x1[qq] - m[qq])));
+      l[qq] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2v, 0x3F803F80u), l[qq], false);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[qq][e] = fmaf(p, v[e], acc[qq][e]);
+      for (int e = 0; e < DPL; ++e)
+        acc[qq][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2v, vp[e]), acc[qq][e], false);
     }
   };
-  for (int j = kb; j < ke; j += kPF) {
-#pragma unroll
-    for (int u = 0; u < kPF; ++u) {
-      if (j + u < ke) {                                  // uniform per wavefront
-        const int jn = j + u + kPF - 1;
-        if (row_ok && jn < ke) {
-          load_slice<D>(kr[(u + kPF - 1) % kPF], key_row(jn, rkb, knb), g);
-          load_slice<D>(vr[(u + kPF - 1) % kPF], key_row(jn, rvb, vnb), g);
-        }
-        process(j + u, kr[u], vr[u]);
-      }
+  auto refill = [&](int u, int jn) {
+    if (row_ok && jn < ke) {
+      load_slice<D>(kr[u], key_row(jn, rkb, knb), g);
+      load_slice<D>(vr[u], key_row(jn, rvb, vnb), g);
+    }
+  };
+  for (int j = kb; j < ke; j += kPF) {                   // bounds are uniform per wavefront
+    process2(j, kr[0], vr[0], kr[1], vr[1], j + 1 < ke);
+    refill(0, j + 4);
+    refill(1, j + 5);
+    if (j + 2 < ke) {
+      process2(j + 2, kr[2], vr[2], kr[3], vr[3], j + 3 < ke);
+      refill(2, j + 6);
+      refill(3, j + 7);
     }
   }
 
