@@ -331,3 +331,58 @@ def test_staged_other_shapes(ca2, sh):
         fw += n
         assert cache.ca2_cache_slot_map() == oq.slot_map()
     cache.close()
+
+
+def test_random_mixed_write_paths(ca2):
+    """Seeded random sequences on a cache with staging slots: each chunk (random
+    size 1..l) goes in either by the copy path (ca2_cache_write) or by the fused
+    stage + commit, so the two placements interleave through eviction and ring
+    wrap. After every write the slot map equals the oracle queue's, and a
+    denoising call's temporal and prefix spatial attention match the oracle
+    over the oracle's own cached K/V."""
+    sh = dict(B=1, H=2, d=64, S=24, l=4, p_max=6, p_spatial=2, tpe_len=10, dtype="bf16")
+    B, S, H, d, l, P, Ps = sh["B"], sh["S"], sh["H"], sh["d"], sh["l"], sh["p_max"], sh["p_spatial"]
+    c_in = 64
+    rng = np.random.default_rng(99)
+    w, rows = _weights(sh, c_in, 37)
+    dw, drows = to_dev(w, "bf16"), torch.from_numpy(rows.astype(np.float32)).cuda()
+    cache = ca2.Cache.from_shape(sh, staged=True)
+    oq, osp = TemporalQueue(P, slots=P + l), SpatialCache(Ps)
+    okf, ovf = {}, {}
+    fw = 0
+    for step in range(14):
+        n = 1 if step == 0 else int(rng.integers(1, l + 1))
+        if rng.random() < 0.5:
+            x = _inputs(sh, c_in, 13, n, step)
+            exact = [_split(t, sh, n) for t in qkv_proj_tpe_ref(x, w, rows, fw, n, S)]
+            k_ref, v_ref = _bf16(exact[1]), _bf16(exact[2])
+            cache.ca2_qkv_proj_stage(to_dev(x, "bf16").view(B, n, S, c_in), dw, drows)
+            cache.ca2_cache_commit()
+            path = "staged"
+        else:
+            k_ref = synth.frames_tensor(14, "kt", range(fw, fw + n), B, S, H, d, "bf16").astype(np.float64)
+            v_ref = synth.frames_tensor(14, "vt", range(fw, fw + n), B, S, H, d, "bf16").astype(np.float64)
+            dk, dv = to_dev(k_ref.astype(np.float32), "bf16"), to_dev(v_ref.astype(np.float32), "bf16")
+            cache.ca2_cache_write(dk, dv, dk, dv)
+            path = "copy"
+        oq.write(range(fw, fw + n))
+        osp.write(range(fw, fw + n))
+        for f in range(n):
+            okf[fw + f], ovf[fw + f] = k_ref[:, f], v_ref[:, f]
+        fw += n
+        assert cache.ca2_cache_slot_map() == oq.slot_map(), f"step {step} ({path})"
+        q, k, v = (synth.step_tensor(15, nm, step, 0, B, l, S, H, d, "bf16") for nm in ("q", "k", "v"))
+        dq, dk, dv = (to_dev(t, "bf16") for t in (q, k, v))
+        ot, os_ = torch.empty_like(dq), torch.empty_like(dq)
+        cache.ca2_temporal_attn(dq, dk, dv, ot)
+        cache.ca2_spatial_attn(dq, dk, dv, os_)
+        torch.cuda.synchronize()
+        ids = oq.frame_ids()
+        rk, rv = np.stack([okf[f] for f in ids], 1), np.stack([ovf[f] for f in ids], 1)
+        check_close(to_host(ot), temporal_attn_ref(q, k, v, rk, rv, list(range(len(ids))), d ** -0.5), "bf16",
+                    f"step {step} ({path}) temporal")
+        pf = osp.logical_frames()
+        ks, vs = np.stack([okf[f] for f in pf], 1), np.stack([ovf[f] for f in pf], 1)
+        check_close(to_host(os_), spatial_attn_ref(q, k, v, ks, vs, list(range(Ps)), d ** -0.5, "prefix"), "bf16",
+                    f"step {step} ({path}) spatial")
+    cache.close()
