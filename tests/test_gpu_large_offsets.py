@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from oracle import temporal_attn_ref, spatial_attn_ref
-from gpu_util import to_host, check_close
+from gpu_util import to_dev, to_host, check_close
 
 pytestmark = pytest.mark.gpu
 
@@ -71,4 +71,48 @@ def test_ring_beyond_4gib(ca2):
                                  vh[sl][:, :, :, h:h + 1], ks_h[:, :, :, h:h + 1], vs_h[:, :, :, h:h + 1],
                                  list(range(P_SP)), d ** -0.5, "prefix")
         check_close(oh[sl][:, :, toks][:, :, :, h:h + 1], ref_s, "bf16", f"spatial frame {f} head {h}")
+    cache.close()
+
+
+def test_staged_write_beyond_4gib(ca2):
+    """The fused cache-writing stage on a ring of 488 slots (9.2 GB of K/V):
+    after 481 frames the next chunk's slots start 4.5 GB into the ring, so
+    the epilogue's ring offsets are beyond 32 bits. The write-pass temporal
+    attention reading the staged frames from those slots must equal, bit for
+    bit, the same call given the caller's K/V outputs; sampled projection rows
+    match the oracle (bf16 bar)."""
+    from oracle import qkv_proj_tpe_ref
+    import synth
+    C = H * d
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261)
+    cache = ca2.Cache(B, H, d, S, L, P_MAX, P_SP, P_MAX + L, "bf16", staged=True)
+    info = cache.ca2_cache_info_get()
+    assert info["ring_slots"] == P_MAX + L and info["bytes_resident"] > 2 ** 33
+    for n in [1] + [L] * 60:
+        t = torch.randn((B, n, S, H, d), generator=gen, device="cuda").to(torch.bfloat16)
+        cache.ca2_cache_write(t, t, t, t)
+    fw = cache.ca2_cache_info_get()["frames_written"]
+    assert fw == 481
+    frame_bytes = S * C * 2
+    assert (fw % (P_MAX + L)) * frame_bytes > 2 ** 32          # the staged slots lie past 4 GiB
+    x = synth.normal(5, "x", (3, 9, 1, L, S, 64), (B * L * S, 64), "bf16")
+    w = synth.weight(5, 3 * C, 64, 0.05)
+    rows = synth.normal(5, "w", (4, P_MAX + L, 3 * C), (P_MAX + L, 3 * C), "f32", std=0.5)
+    dq, dk, dv = (torch.empty((B, L, S, H, d), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    cache.ca2_qkv_proj_stage(to_dev(x, "bf16").view(B, L, S, 64), to_dev(w, "bf16"),
+                             torch.from_numpy(rows).cuda(), dq, dk, dv)
+    out_ring, out_own = torch.empty_like(dq), torch.empty_like(dq)
+    cache.ca2_temporal_attn(dq, None, None, out_ring)
+    cache.ca2_temporal_attn(dq, dk, dv, out_own)
+    torch.cuda.synchronize()
+    assert torch.equal(out_ring.view(torch.int16), out_own.view(torch.int16))
+    got = torch.cat([t.view(-1, C) for t in (dq, dk, dv)], 1)
+    for f in (0, 7):
+        r0 = f * S + 1000                                         # 48 tokens of frame f
+        ref = np.concatenate(qkv_proj_tpe_ref(x[r0:r0 + 48], w, rows, fw + f, 1, 48), 1)
+        check_close(to_host(got[r0:r0 + 48]), ref, "bf16", f"frame {f} rows")
+    cache.ca2_cache_commit()
+    info = cache.ca2_cache_info_get()
+    assert info["p_k"] == P_MAX and info["frames_written"] == fw + L
     cache.close()
