@@ -8,7 +8,10 @@
 // bidirectional temporal attention of the recompute baseline (abstract page:
 // problem statement; notes: speed comparison with OS-Ext).
 //
-// Work mapping (HBM-bound: each K/V byte is used by at most n queries):
+// Two kernels. bf16 caches use the dimension-split kernel further down (K/V
+// streamed from HBM straight into registers). fp32 caches use this one.
+// Work mapping of the fp32 kernel (HBM-bound: each K/V byte is used by at
+// most n queries):
 //   * a wavefront owns ROWS = 64/QL consecutive rows; lane = (row, query),
 //     QL = lanes per row >= n, so the n queries of a row sit in adjacent
 //     lanes and read the same staged key row (LDS broadcast);
@@ -259,10 +262,13 @@ __global__ __launch_bounds__(64 * kWaves) void temporal_attn_kernel(TemporalArgs
 // dword = 18 dims), so every load is aligned and the quad covers the row.
 // q.k is a v_dot2_f32_bf16 partial sum reduced across the quad with two DPP
 // adds; the softmax statistics and the accumulators for the lane's dims stay
-// in registers. The next key's K/V slice is loaded while the current key is
-// processed. The running maximum is only raised when a score exceeds it by
-// more than 2^8 (base-2 units), so the accumulators are rescaled a handful of
-// times per row instead of once per key.
+// in registers. Keys are taken in pairs from a 4-slot register ring (one
+// pair in flight while the other is processed): the pair's P is rounded to
+// bf16 and O += P V is one v_dot2_f32_bf16 per dimension and query over the
+// two keys (fp32 accumulate), the normaliser the same dot product with (1, 1).
+// The running maximum is only raised when a score exceeds it by more than
+// 2^8 (base-2 units), so the accumulators are rescaled a handful of times per
+// row instead of once per key.
 // When rows are few, the key range is split over up to 4 wavefronts of a
 // workgroup and the partial results are merged through LDS.
 
