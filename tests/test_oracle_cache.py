@@ -177,3 +177,27 @@ def test_queue_without_staging_slots_overwrites_queued_frames():
     q.write(range(5))
     before = set(q.slot_map())
     assert before & set(q.write(range(5, 7)))
+
+
+def test_staging_slots_property():
+    """Random P_max, chunk length and write sequences (each write 1..l frames):
+    with P_max + l physical slots every write lands in slots that held no
+    queued frame, and placement always equals the brute-force ring."""
+    import hypothesis
+    import hypothesis.strategies as st
+
+    @hypothesis.settings(max_examples=120, deadline=None, derandomize=True)
+    @hypothesis.given(p_max=st.integers(1, 12), l=st.integers(1, 6), data=st.data())
+    def check(p_max, l, data):
+        writes = data.draw(st.lists(st.integers(1, l), min_size=1, max_size=12))
+        q = TemporalQueue(p_max, slots=p_max + l)
+        total = 0
+        for w in writes:
+            before = set(q.slot_map())
+            landed = q.write(range(total, total + w))
+            total += w
+            assert not before & set(landed)
+            ids, slots = _brute_force_ring_slots(p_max, p_max + l, total)
+            assert q.frame_ids() == ids and q.slot_map() == slots
+
+    check()
