@@ -112,3 +112,33 @@ def test_errors_on_device(ca2):
     assert raw.ca2_cache_write(cache.handle, x.data_ptr(), x.data_ptr(), None, None, 4, None) == ca2.CA2_ERR_INVALID_ARG
     # nothing was written by the failed calls
     assert cache.ca2_cache_info_get()["frames_written"] == 0
+
+
+def test_calls_on_a_side_stream_match_the_default_stream(ca2):
+    """Every entry point runs on the caller's stream: the same writes and
+    denoising calls issued on a side stream (default priority) and on the
+    default stream give bit-identical caches and outputs."""
+    sh = dict(B=1, H=4, d=72, S=64, l=8, p_max=9, p_spatial=3, tpe_len=17, dtype="bf16")
+    outs, dumps = [], []
+    side = torch.cuda.Stream()
+    for stream in (None, side):
+        cache = ca2.Cache.from_shape(sh)
+        o = RolloutOracle(sh, 21)
+        ctx = torch.cuda.stream(stream) if stream is not None else torch.cuda.stream(torch.cuda.current_stream())
+        with ctx:
+            for w in (1, 8, 8):
+                fr = o.next_frames(w)
+                cache.ca2_cache_write(*(to_dev(o.clean(x, fr), "bf16") for x in ("kt", "vt", "ks", "vs")))
+                o.write(fr)
+            q, k, v = (to_dev(o.noisy(x, 2, 7, 8), "bf16") for x in ("q", "k", "v"))
+            ot, os_ = torch.empty_like(q), torch.empty_like(q)
+            cache.ca2_spatial_attn(q, k, v, os_)
+            cache.ca2_temporal_attn(q, k, v, ot)
+        torch.cuda.synchronize()
+        outs.append((ot.view(torch.int16).cpu(), os_.view(torch.int16).cpu()))
+        dumps.append(cache.ca2_cache_debug_copy())
+        cache.close()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+    for a, b in zip(dumps[0], dumps[1]):
+        assert np.array_equal(a, b)
