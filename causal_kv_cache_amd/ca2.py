@@ -26,6 +26,7 @@ CA2_SPATIAL_PREFIX = 0
 CA2_SPATIAL_SELF = 1
 CA2_STAGE_RING = 1
 CA2_STAGE_SPATIAL = 2
+ABI_VERSION = 2      # include/ca2.h CA2_ABI_VERSION this binding is written for
 
 _DTYPES = {"f32": CA2_F32, "bf16": CA2_BF16}
 
@@ -75,6 +76,7 @@ _SIGS = {
     "ca2_toy_temb_mod": (_I32, [_P, _I32, _P, _I32, _I32, _P, _P]),
     "ca2_toy_ln_mod": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P]),
     "ca2_toy_linear": (_I32, [_P, _I32, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _P]),
+    "ca2_abi_version": (_I32, []),
     "ca2_status_string": (ctypes.c_char_p, [_I32]),
     "ca2_last_error": (ctypes.c_char_p, []),
 }
@@ -104,6 +106,13 @@ def load():
     except ImportError:
         pass
     lib = ctypes.CDLL(LIB_PATH)
+    if not hasattr(lib, "ca2_abi_version"):
+        raise RuntimeError(f"{LIB_PATH} predates the ABI version check: rebuild it")
+    lib.ca2_abi_version.restype = _I32
+    lib.ca2_abi_version.argtypes = []
+    if lib.ca2_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {lib.ca2_abi_version()}, this binding expects "
+                           f"{ABI_VERSION}: rebuild it from these sources")
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)
         fn.restype = res

@@ -157,6 +157,8 @@ const char* ca2_status_string(int32_t s) {
 
 const char* ca2_last_error(void) { return g_last_error.c_str(); }
 
+int32_t ca2_abi_version(void) { return CA2_ABI_VERSION; }
+
 uint64_t ca2_bytes_resident(const ca2_config* cfg) {
   if (check_config(cfg) != CA2_OK) return 0;
   const uint64_t frame = (uint64_t)cfg->tokens * cfg->heads * cfg->head_dim * elem_bytes(cfg->dtype);

@@ -333,6 +333,12 @@ ca2_status ca2_toy_linear(const float* x, int32_t ldx, const float* w, int32_t l
                           int32_t ldr, float* y, int32_t ldy, int32_t m, int32_t n, int32_t k,
                           int32_t act, void* stream);
 
+/* Version of this ABI (entry points, argument lists, struct layouts):
+ * CA2_ABI_VERSION. A binding compares it with the value it was written for
+ * and refuses a library built from other sources. */
+#define CA2_ABI_VERSION 2
+int32_t ca2_abi_version(void);
+
 /* Static description of a status code; any other integer gives
  * "unknown status". Takes a plain integer so that codes from any caller,
  * valid or not, are well defined. */

@@ -70,6 +70,8 @@ int main() {
   CHECK(ca2_bytes_resident(&c) == 0);
   CHECK(ca2_bytes_resident(nullptr) == 0);
 
+  CHECK(ca2_abi_version() == CA2_ABI_VERSION);
+
   // status strings
   for (int32_t s = 0; s <= 5; ++s) CHECK(std::strlen(ca2_status_string(s)) > 0);
   CHECK(std::strcmp(ca2_status_string(99), "unknown status") == 0);

@@ -186,3 +186,12 @@ def test_slot_maps_random_write_sequences(lib):
             assert lib.ca2_tpe_index_raw(fw, 16, L) == tpe_index_ref(fw, 16, L)
 
     check()
+
+
+def test_abi_version_matches_header(lib):
+    """The library reports the ABI version the header declares, and the
+    binding was written for the same one."""
+    import re
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ca2.h")).read()
+    declared = int(re.search(r"#define CA2_ABI_VERSION (\d+)", hdr).group(1))
+    assert lib.load().ca2_abi_version() == declared == lib.ABI_VERSION
