@@ -479,6 +479,7 @@ ca2_status ca2_qkv_proj(const void* x, const void* w, void* q, void* k, void* v,
   if (m < 1 || c_in < 64 || c_out < 64 || c_in % 64 || c_out % 64)
     return fail(CA2_ERR_INVALID_ARG, "m >= 1, c_in and c_out multiples of 64");
   if (m > 0x7fffff00) return fail(CA2_ERR_INVALID_ARG, "m too large");   // token index + tile stays in int32
+  if (c_in > (1 << 20) || c_out > (1 << 20)) return fail(CA2_ERR_INVALID_ARG, "c_in, c_out <= 2^20");
   if ((int64_t)m * c_in > ((int64_t)1 << 40)) return fail(CA2_ERR_INVALID_ARG, "too large");
   ca2::ProjArgs a;
   memset(&a, 0, sizeof(a));
@@ -502,8 +503,9 @@ ca2_status ca2_qkv_proj_stage(ca2_cache* c, const void* x, const void* w, const 
     return fail(CA2_ERR_INVALID_ARG, "targets %d: a nonempty combination of CA2_STAGE_RING, CA2_STAGE_SPATIAL",
                 targets);
   const int32_t c_out = c->cfg.heads * c->cfg.head_dim;
-  if (c_in < 64 || c_in % 64 || c_out % 64)
-    return fail(CA2_ERR_INVALID_ARG, "c_in (%d) and heads * head_dim (%d) must be multiples of 64", c_in, c_out);
+  if (c_in < 64 || c_in % 64 || c_out % 64 || c_in > (1 << 20))
+    return fail(CA2_ERR_INVALID_ARG, "c_in (%d, at most 2^20) and heads * head_dim (%d) must be multiples of 64",
+                c_in, c_out);
   const int64_t m = (int64_t)c->cfg.batch * n * c->cfg.tokens;
   if (m > 0x7fffff00 || m * c_in > ((int64_t)1 << 40)) return fail(CA2_ERR_INVALID_ARG, "too large");
   if ((targets & CA2_STAGE_RING) && c->ring_slots < c->cfg.p_max + n)

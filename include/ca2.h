@@ -257,7 +257,7 @@ ca2_status ca2_cache_debug_copy(const ca2_cache* cache, void* host_k, void* host
  * that are stored). x: [m][c_in] bf16 tokens; w: [3*c_out][c_in] bf16,
  * row-major weight of a linear layer; q, k, v: [m][c_out] bf16 outputs =
  * columns [0,c), [c,2c), [2c,3c) of x * w^T, accumulated in float32.
- * m >= 1; c_in and c_out multiples of 64.
+ * m >= 1; c_in and c_out multiples of 64, at most 2^20.
  */
 ca2_status ca2_qkv_proj(const void* x, const void* w, void* q, void* k, void* v,
                         int32_t m, int32_t c_in, int32_t c_out, void* stream);

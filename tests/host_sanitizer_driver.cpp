@@ -142,6 +142,7 @@ int main() {
   CHECK(ca2_temporal_attn_frames(p, p, p, p, 1, 4, 16, 2, 16, CA2_BF16, 0, 0.125f, nullptr) == CA2_ERR_UNSUPPORTED);
   CHECK(ca2_spatial_attn_frames(p, p, p, nullptr, 1, 4, 16, 2, 64, CA2_BF16, 0.125f, nullptr) == CA2_ERR_INVALID_ARG);
   CHECK(ca2_qkv_proj(p, p, p, p, p, 8, 65, 64, nullptr) == CA2_ERR_INVALID_ARG);
+  CHECK(ca2_qkv_proj(p, p, p, p, p, 8, 1 << 21, 64, nullptr) == CA2_ERR_INVALID_ARG);
   const float* fp = reinterpret_cast<const float*>(p);
   float* fo = reinterpret_cast<float*>(p);
   CHECK(ca2_toy_temb_mod(fp, 2, fp, 7, 32, fo, nullptr) == CA2_ERR_INVALID_ARG);
