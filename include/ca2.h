@@ -284,7 +284,7 @@ ca2_status ca2_qkv_proj(const void* x, const void* w, void* q, void* k, void* v,
  * The frames stay staged: the queue and the frame count do not move until
  * ca2_cache_commit, so the chunk's temporal attention still sees the queue
  * before eviction (pass k_new = v_new = NULL to read the new frames from the
- * ring). Bf16 caches only; c_in and C multiples of 64.
+ * ring). Bf16 caches only; c_in and C multiples of 64, c_in at most 2^20.
  * Errors: INVALID_ARG (NULL x/w, misaligned pointer, bad sizes or targets),
  * STATE (ring target without staging slots; a target already staged, or a
  * different n, since the last commit), UNSUPPORTED (fp32 cache), HIP.
