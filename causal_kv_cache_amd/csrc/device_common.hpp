@@ -84,12 +84,20 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
 
 // 16-byte global -> LDS copy for every active lane: lane i reads
 // sbase + voff (+ 0..15) and writes lds_addr + 16*i (lds_addr in M0);
-// sbase and lds_addr are wavefront-uniform.
+// sbase and lds_addr are wavefront-uniform. The instruction writes LDS only
+// (no register result), and the kernels that use it wait for it with
+// explicit vmcnt counts. M0 is a register the compiler reserves, so it warns
+// that the clobber may not be honoured; in the kernels built here every M0
+// reference in the generated code is this one (no indirect register moves,
+// messages or GWS operations), so nothing of the compiler's lives in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16s(unsigned voff, uint64_t sbase, unsigned lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(uniform64(sbase)), "s"((unsigned)__builtin_amdgcn_readfirstlane((int)lds_addr))
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Block index -> work index such that XCD x (which receives blocks x, x+8,
 // x+16, ...) processes work items [start_x, start_x + count_x) in order.

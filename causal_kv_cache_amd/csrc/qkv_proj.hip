@@ -61,7 +61,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int w = xcd_work_index(blockIdx.x, gridDim.x);
   const int n0 = (w % tiles_n) * TN;
   const int m0 = (w / tiles_n) * TM;
-  const bool edge = n0 + TN > N || m0 + TM > a.m;   // rows past the matrices: masked copies
   const int KT = a.c_in / TK;
 
   // per-lane copy offsets (bytes from the k-tile base) for this wavefront's

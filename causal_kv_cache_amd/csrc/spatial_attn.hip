@@ -128,7 +128,9 @@ __device__ __forceinline__ void lazy_rescale(float mx_raw, float c, float& m_run
 // barrier, refills the stage of tile t-1 with tile t+kStages-1.
 
 template <int D, int QB, int kSW, bool FULL, int kStages, int KS>
-__global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(2, 8))) void spatial_attn_pipe_kernel(SpatialArgs a) {
+// (d > 72: the ring of one workgroup takes most of the CU's LDS, so one
+// wavefront per SIMD is all that can be resident)
+__global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(D <= 72 ? 2 : 1, 8))) void spatial_attn_pipe_kernel(SpatialArgs a) {
   using C = SCfg<D, kSW>;
   static_assert(KS == 1 || KS == 2, "key split over one or two wavefronts");
   constexpr int G = kSW / KS;                      // query groups of 32*QB per workgroup
