@@ -23,7 +23,8 @@ struct TemporalArgs {
   int32_t n;               // new frames (queries per row)
   int32_t p_k;             // queued frames
   int32_t head;            // ring slot of the oldest queued frame
-  int32_t p_max;           // ring slots (the modulus of the slot arithmetic)
+  int32_t p_max;           // ring slots R (the modulus of the slot arithmetic): P_max, or
+                           // P_max + chunk for a cache with staging slots
   int32_t ring_keys;       // keys 0..ring_keys-1 are read from ring slots (head + j) mod p_max:
                            // p_k, or p_k + n when the new frames were already written
                            // into the slots after the queue (k_new / v_new unused)

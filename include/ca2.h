@@ -133,7 +133,7 @@ void ca2_cache_destroy(ca2_cache* cache);
  * k_s, v_s: spatial-layer K/V of the same frames, [B][n][S][H][d]; may be
  *           NULL only when p_spatial == 0.
  * Appends the frames to the temporal queue -- frame F goes to ring slot
- * F mod P_max, which is the slot right after the newest queued frame -- and,
+ * F mod R, which is the slot right after the newest queued frame -- and,
  * past P_max, drops the oldest frames (FIFO eviction, [notes] key design 4).
  * An over-full write is the normal case, not an error. Keeps the last P'
  * clean frames in the spatial buffer (frame F at slot F mod P'). Copies are
