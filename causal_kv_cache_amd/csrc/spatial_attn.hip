@@ -21,6 +21,7 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 
+#include <atomic>
 #include <cstdlib>
 
 namespace ca2 {
@@ -116,7 +117,11 @@ __device__ __forceinline__ void lazy_rescale(float mx_raw, float c, float& m_run
 // d that turns row d of the PV accumulator into the softmax row sum) are
 // written once at the start and never copied over (their lanes are masked).
 // A wavefront waits only for its own copies of the tile it needs (s_waitcnt
-// vmcnt), then one barrier per tile publishes it.
+// vmcnt), then one barrier per tile publishes it. With PROD an extra
+// wavefront issues every copy and does that wait alone: a copy instruction
+// holds its wavefront for as long as the CU's memory pipeline takes to accept
+// 64 x 16 bytes, and that time then no longer falls on the wavefronts that
+// compute, which only take the barrier.
 //
 // Compute: each wavefront cuts a tile into two chunks of 32 keys and, with
 // S(c) the scores of chunk c, overlaps
@@ -127,12 +132,14 @@ __device__ __forceinline__ void lazy_rescale(float mx_raw, float c, float& m_run
 // iteration t a wavefront waits for its copies of tile t+1 and, after the
 // barrier, refills the stage of tile t-1 with tile t+kStages-1.
 
-template <int D, int QB, int kSW, bool FULL, int kStages, int KS>
+template <int D, int QB, int kSW, bool FULL, int kStages, int KS, bool PROD>
 // (d > 72: the ring of one workgroup takes most of the CU's LDS, so one
 // wavefront per SIMD is all that can be resident)
-__global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(D <= 72 ? 2 : 1, 8))) void spatial_attn_pipe_kernel(SpatialArgs a) {
-  using C = SCfg<D, kSW>;
+__global__ __launch_bounds__(64 * (kSW + PROD)) __attribute__((amdgpu_waves_per_eu(D <= 72 ? 2 : 1, 8))) void spatial_attn_pipe_kernel(SpatialArgs a) {
+  using C = SCfg<D, PROD ? 1 : kSW>;
   static_assert(KS == 1 || KS == 2, "key split over one or two wavefronts");
+  static_assert(!PROD || KS == 1, "a copy wavefront only with one key range per wavefront");
+  constexpr int kThreads = 64 * (kSW + PROD);
   constexpr int G = kSW / KS;                      // query groups of 32*QB per workgroup
   static_assert(kStages >= 3, "the pipeline reads tile t+1 while tile t+2 is copied");
   constexpr int KSTEPS = C::KSTEPS, DBLK = C::DBLK, KSL = C::KSL, VSL = C::VSL, CH = C::CH;
@@ -142,6 +149,10 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(D <= 7
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // PROD: wavefront kSW issues every copy and computes nothing
+  const bool producer = PROD && wave == kSW;
+  const int cw = PROD ? 0 : wave;                  // copy instructions cw, cw + CSW, ...
+  constexpr int CSW = PROD ? 1 : kSW;
   const int half = lane >> 5;
   const int col = lane & 31;
   const int S = a.tokens;
@@ -168,7 +179,7 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(D <= 7
     for (int s = 0; s < KSTEPS; ++s) {
       const int d0 = 16 * s + 8 * half;
       uint4 u = make_uint4(0, 0, 0, 0);
-      if (q_ok[qb] && d0 < D) u = *reinterpret_cast<const uint4*>(qp + d0);
+      if (!producer && q_ok[qb] && d0 < D) u = *reinterpret_cast<const uint4*>(qp + d0);
       qop[qb][s] = __builtin_bit_cast(bf16x8v, u);
     }
   }
@@ -178,14 +189,14 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(D <= 7
   // Partial tiles also leave key rows uncopied, so without full tiles the
   // whole ring starts zeroed.
   if constexpr (!FULL) {
-    for (int i = tid; i < kStages * C::STAGE / 16; i += 64 * kSW)
+    for (int i = tid; i < kStages * C::STAGE / 16; i += kThreads)
       reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
   }
   {
     constexpr int KP = KSL - CH, VP = VSL - CH;           // padding slots per row
     constexpr int PER = kBN * (KP + VP) + 6;              // + 32 B after K, 64 B after V
-    for (int i = tid; i < kStages * PER; i += 64 * kSW) {
+    for (int i = tid; i < kStages * PER; i += kThreads) {
       const int st = i / PER, k = i % PER;
       int off;
       bool ones = false;
@@ -206,14 +217,14 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(D <= 7
   if constexpr (!FULL) __syncthreads();   // ones land before any copy into the zeroed ring
   // copy stream: per-lane byte offsets of each of this wavefront's copy
   // instructions from the tile base (tile-independent), padding lanes masked
-  const int n_mine = (C::NI - wave + kSW - 1) / kSW;
+  const int n_mine = (C::NI - cw + CSW - 1) / CSW;
   const unsigned row_bytes = (unsigned)(tok_stride * 2);
   unsigned g_off[MAXI];
   int g_row[MAXI];
   bool g_pad[MAXI];
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
-    const int j = wave + kSW * i;
+    const int j = cw + CSW * i;
     const bool isv = j >= KSL;
     const int slot = (isv ? j - KSL : j) * 64 + lane;
     const int row = slot / (isv ? VSL : KSL), c = slot % (isv ? VSL : KSL);
@@ -253,7 +264,7 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(D <= 7
     const int nk = S - t0_c;
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
-      const int j = wave + kSW * i;
+      const int j = cw + CSW * i;
       if (j < C::NI) {                                  // uniform per wavefront
         const bool isv = j >= KSL;
         const unsigned dst = st + (isv ? C::V_OFF + (j - KSL) * 1024 : j * 1024);
@@ -371,11 +382,23 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(D <= 7
   // tiles 0 .. kStages-2 are all requested before the first wait; loads
   // complete in issue order, so once only the younger tiles' copies are
   // outstanding, Q (loaded first) and tile 0 have arrived
-  issue_next();
-  int pre = 0;
-  for (int t = 1; t <= kStages - 2 && t < n_tiles; ++t, ++pre) issue_next();
-  wait_tiles(pre);
+  if (!PROD || producer) {
+    issue_next();
+    int pre = 0;
+    for (int t = 1; t <= kStages - 2 && t < n_tiles; ++t, ++pre) issue_next();
+    wait_tiles(pre);
+  }
   lds_barrier();
+  if constexpr (PROD) {
+    if (producer) {   // the same barriers as the loop below, one per tile
+      for (int t = 0; t + 1 < n_tiles; ++t) {
+        wait_tiles(min(kStages - 3, n_tiles - t - 2));
+        lds_barrier();
+        if (t + kStages - 1 < n_tiles) issue_next();
+      }
+      return;
+    }
+  }
   f32x16 s0[QB], s1[QB];
   bf16x8v pf[QB][2];
   int nk_t = min(kBN, S);             // keys in tile t
@@ -396,9 +419,10 @@ __global__ __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(D <= 7
       if (!FULL && nk_t < kBN) mask_tail(s1, 1, nk_t);
       max_rescale(s1);
       st_r = st_r == kStages - 1 ? 0 : st_r + 1;
-      wait_tiles(min(kStages - 3, n_tiles - t - 2));   // tile t+1; younger tiles stay in flight
+      if constexpr (!PROD) wait_tiles(min(kStages - 3, n_tiles - t - 2));   // tile t+1; younger tiles stay in flight
       lds_barrier();                                    // every wavefront is done with tile t-1
-      if (t + kStages - 1 < n_tiles) issue_next();      // into tile t-1's stage
+      if constexpr (!PROD)
+        if (t + kStages - 1 < n_tiles) issue_next();    // into tile t-1's stage
       // chunk 2t+2 (next tile) is scored while chunk 2t+1 is exponentiated
       qk(smem + st_r * C::STAGE, 0, s0);
       expc(s1, pf);
@@ -582,16 +606,30 @@ __global__ __launch_bounds__(64) void spatial_attn_f32_kernel(SpatialArgs a) {
   }
 }
 
-template <int D, int QB, int SW, int ST, int KS>
+template <int D, int QB, int SW, int ST, int KS, bool PROD = false>
 hipError_t launch_pipe_cfg(const SpatialArgs& a, hipStream_t s) {
   constexpr int BM = 32 * QB * SW / KS;
   const int64_t nwg = (int64_t)((a.tokens + BM - 1) / BM) * a.n * a.heads * a.batch;
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 block(64 * (SW + PROD));
   if (a.tokens % kBN == 0)
-    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, true, ST, KS>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
+    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, true, ST, KS, PROD>), dim3((unsigned)nwg), block, 0, s, a);
   else
-    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, false, ST, KS>), dim3((unsigned)nwg), dim3(64 * SW), 0, s, a);
+    hipLaunchKernelGGL((spatial_attn_pipe_kernel<D, QB, SW, false, ST, KS, PROD>), dim3((unsigned)nwg), block, 0, s, a);
   return hipGetLastError();
+}
+
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 template <int D>
@@ -602,18 +640,25 @@ hipError_t launch_mfma(const SpatialArgs& a, hipStream_t s) {
   // ring: at 256 tokens 3 stages time faster launched alone (18.5 vs 19.7 us)
   // but slower in the denoising step that alternates with the temporal kernel
   // (1.86 vs 1.80 ms per step); 5 and 6 stages take 23.5 us.
-  // CA2_SPATIAL_CFG=1|2|3 forces 32 queries, 64 queries, or 8 wavefronts of
+  // At d = 72 with at most one workgroup per CU the 4 x 32 form gets a fifth
+  // wavefront that issues every copy: the compute wavefronts no longer stall
+  // on copy issue (256-token shape 18.6 -> 17.3 us). With two workgroups per
+  // CU, or at d = 64 / 128 (SGPR and VGPR spills under the two-wavefront
+  // register cap), it measured slower.
+  // CA2_SPATIAL_CFG=1|2|3|4 forces 32 queries, 64 queries, 8 wavefronts of
   // 32 queries x 2 key halves (two wavefronts per SIMD even at one workgroup
   // per CU; measured slower than 4 x 32 at the 256-token shape, kept
-  // selectable).
+  // selectable), or 32 queries with the copy wavefront.
   const int64_t frames = (int64_t)a.n * a.heads * a.batch;
   const int64_t wg_big = (int64_t)((a.tokens + 255) / 256) * frames;
-  int cfg = wg_big >= 1024 ? 2 : 1;
+  const int64_t wg_small = (int64_t)((a.tokens + 127) / 128) * frames;
+  int cfg = wg_big >= 1024 ? 2 : D == 72 && wg_small <= device_cus() ? 4 : 1;
   if (const char* force = getenv("CA2_SPATIAL_CFG")) cfg = force[0] - '0';
   if constexpr (D <= 72) {
     if (cfg == 2) return launch_pipe_cfg<D, 2, 4, 4, 1>(a, s);
   }
   if (cfg == 3) return launch_pipe_cfg<D, 1, 8, 4, 2>(a, s);
+  if (cfg == 4) return launch_pipe_cfg<D, 1, 4, 4, 1, true>(a, s);
   return launch_pipe_cfg<D, 1, 4, 4, 1>(a, s);
 }
 

@@ -209,14 +209,15 @@ FULL_TILE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", ["1", "2", "3"])
+@pytest.mark.parametrize("cfg", ["1", "2", "3", "4"])
 @pytest.mark.parametrize("name,sh,writes,n,mode",
                          [c for c in SPATIAL_CASES if c[1]["dtype"] == "bf16"] + FULL_TILE_CASES,
                          ids=[c[0] for c in SPATIAL_CASES if c[1]["dtype"] == "bf16"] + [c[0] for c in FULL_TILE_CASES])
 def test_spatial_parity_every_launch_variant(ca2, monkeypatch, cfg, name, sh, writes, n, mode):
     """Every bf16 launch variant (4 wavefronts x 32 queries, 4 x 64 queries,
-    8 wavefronts = 4 x 32 queries x 2 key halves) against the oracle,
-    whatever the grid size would pick."""
+    8 wavefronts = 4 x 32 queries x 2 key halves, 4 x 32 queries plus a
+    wavefront that issues every copy) against the oracle, whatever the grid
+    size would pick."""
     if cfg == "2" and sh["d"] > 72:
         pytest.skip("64-query wavefronts are built for d <= 72 only")
     monkeypatch.setenv("CA2_SPATIAL_CFG", cfg)
