@@ -7,7 +7,8 @@
 // one-chunk spatial KV buffer.
 //
 // bf16 path = flash attention on MFMA (v_mfma_f32_32x32x16_bf16):
-//   * a workgroup covers 4 wavefronts x 32*QB queries of one (b, frame, head);
+//   * a workgroup covers 4 wavefronts x 32*QB queries of one (b, frame, head)
+//     (at one workgroup per CU, plus a fifth wavefront that only copies);
 //   * per key tile each wavefront computes S^T = K Q^T (keys x queries) so a
 //     lane owns one query column: the softmax row statistics are per lane,
 //     shared with the partner lane (lane ^ 32) by one exchange, and the
