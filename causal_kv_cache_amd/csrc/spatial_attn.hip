@@ -382,7 +382,10 @@ __global__ __launch_bounds__(64 * (kSW + PROD)) __attribute__((amdgpu_waves_per_
   // ---- prologue: tile 0 copied while Q is loaded, tiles 1..kStages-2 in flight, first chunk scored ----
   // tiles 0 .. kStages-2 are all requested before the first wait; loads
   // complete in issue order, so once only the younger tiles' copies are
-  // outstanding, Q (loaded first) and tile 0 have arrived
+  // outstanding, Q (loaded first) and tile 0 have arrived. With PROD the
+  // copy wavefront (which loads no Q) does this wait alone; the compute
+  // wavefronts issue no copies, so the compiler's own waits for their Q
+  // loads are exact.
   if (!PROD || producer) {
     issue_next();
     int pre = 0;
