@@ -250,3 +250,129 @@ def check_tpe_proj_distributive(impl, B=2, S=3, C_in=6, C=3, seed=22):
     want = np.concatenate(qkv_proj_ref(x + per_row, w), 1)
     got = np.concatenate(impl(x, w, e @ w.T, _TPE_FIRST, _TPE_N, S), 1)
     return float(np.max(np.abs(got - want)))
+
+
+# ---------------------------------------------------------------------------
+# toy block layer forms (layer norm, tanh-GELU, sinusoidal timestep
+# embedding, shift/scale modulation): textbook definitions, pinned by the
+# mathematics since the pages do not give the backbone
+# ---------------------------------------------------------------------------
+LN_EPS = 1e-6
+
+
+def check_layernorm(ln, seed=31):
+    """What fixes a layer norm with epsilon 1e-6 over the last axis: every
+    output row has mean 0 and population variance var / (var + 1e-6) (var
+    the row's population variance); a constant row maps to 0; LN(a x + b) =
+    LN(x) for a > 0 up to the epsilon's effect (rows of variance ~1); the
+    hand-worked row [0, 0, 0, 4] (mean 1, variance 3) gives
+    [-1, -1, -1, 3] / sqrt(3 + 1e-6). Returns the worst ratio of a violation
+    to its tolerance (<= 1 passes)."""
+    g = np.random.default_rng(seed)
+    r = []
+    for var_scale in (1e-7, 1e-6, 1e-3, 1.0, 50.0):   # small variances make the epsilon visible
+        x = g.standard_normal((6, 9)) * np.sqrt(var_scale) + g.standard_normal((6, 1))
+        y = ln(x)
+        var = x.var(-1)
+        r.append(float(np.max(np.abs(y.mean(-1)))) / 1e-9)
+        want = var / (var + LN_EPS)
+        r.append(float(np.max(np.abs(y.var(-1) - want) / want)) / 1e-9)
+    r.append(float(np.max(np.abs(ln(np.full((2, 5), 3.25))))) / 1e-12)
+    x = g.standard_normal((4, 16))
+    r.append(float(np.max(np.abs(ln(2.5 * x - 7.0) - ln(x)))) / 1e-5)
+    row = ln(np.array([[0.0, 0.0, 0.0, 4.0]]))
+    want = np.array([-1.0, -1.0, -1.0, 3.0]) / np.sqrt(3.0 + 1e-6)
+    r.append(float(np.max(np.abs(row - want))) / 1e-12)
+    return max(r)
+
+
+GELU_ERF_BOUND = 4.8e-4   # published maximum deviation of the tanh form from x*Phi(x) is ~4.73e-4
+
+
+def check_gelu_tanh(gelu):
+    """Worst violation of what fixes the tanh form of GELU: gelu(0) = 0;
+    gelu(x) - gelu(-x) = x (tanh is odd); |gelu(x) - x Phi(x)| <= 4.8e-4 with
+    Phi from math.erf; the slope of (gelu(x) - x/2) / x^2 at 0 is
+    1/sqrt(2 pi), as for x Phi(x) (fixes the constant sqrt(2/pi) inside the
+    tanh). Returns the worst ratio of violation to its bound (<= 1 passes)."""
+    import math
+    x = np.linspace(-8.0, 8.0, 4001)
+    y = gelu(x)
+    exact = np.array([0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0))) for v in x])
+    r = [abs(float(gelu(np.array([0.0]))[0])) / 1e-15,
+         float(np.max(np.abs(y - gelu(-x) - x))) / 1e-12,
+         float(np.max(np.abs(y - exact))) / GELU_ERF_BOUND]
+    h = 1e-4
+    slope = (float(gelu(np.array([h]))[0]) - h / 2) / h ** 2
+    r.append(abs(slope - 1.0 / math.sqrt(2.0 * math.pi)) / 1e-6)
+    return max(r)
+
+
+def check_timestep_embedding(temb, half):
+    """What fixes the sinusoidal embedding [sin(t w_i) for i < h, cos(t w_i)
+    for i < h], w_i = 1000^(-i/h): emb(0) = [0]*h + [1]*h; sin^2 + cos^2 = 1
+    per frequency at any t; w_0 = 1, so emb(t)[0] = sin t and emb(t)[h] =
+    cos t; the frequencies recovered from a small t by atan2 equal
+    10^(-3i/h) (h = 4: 1, 0.1778279410, 0.0316227766, 0.0056234133). Returns
+    the worst ratio of a violation to its tolerance (<= 1 passes)."""
+    r = [float(np.max(np.abs(temb(0.0) - np.concatenate([np.zeros(half), np.ones(half)])))) / 1e-15]
+    for t in (0.7, 20.0, 900.0):
+        e = temb(t)
+        r.append(float(np.max(np.abs(e[:half] ** 2 + e[half:] ** 2 - 1.0))) / 1e-12)
+        r.append(max(abs(float(e[0]) - np.sin(t)), abs(float(e[half]) - np.cos(t))) / 1e-12)
+    t = 1e-3
+    e = temb(t)
+    w = np.arctan2(e[:half], e[half:]) / t
+    want = np.array([1.0, 0.1778279410, 0.0316227766, 0.0056234133]) if half == 4 else \
+        10.0 ** (-3.0 * np.arange(half) / half)
+    r.append(float(np.max(np.abs(w - want))) / 1e-9)
+    return max(r)
+
+
+def check_toy_modulation(model_factory, gelu, ln, S=3, C=4, seed=33):
+    """The six modulation vectors of a frame (temb(t) @ wmod, split in six)
+    are, in order, shift and scale of the spatial, the temporal and the MLP
+    pre-norm: h = LN(x) (1 + scale) + shift. Pinned on a one-layer block with
+    hand-set weights whose output has a closed form: with Q = K = 0 an
+    attention layer averages its visible values (spatial: the frame's own
+    tokens; temporal: frames 0..f), with the value projection and the output
+    projection the identity its output is that average of the pre-norm h,
+    and with w1 = [I 0], w2 = [I; 0] the MLP adds gelu(h). One layer at a
+    time carries an identity value path (the others are zero), and one of the
+    six vectors at a time is set to `a` through the cos(0 * w_0) = 1 entry of
+    temb(0). Returns the max error against the closed forms."""
+    g = np.random.default_rng(seed)
+    F = 2
+    x = g.standard_normal((F, S, C))
+    a = g.standard_normal(C) * 0.5
+    I = np.eye(C)
+    worst = 0.0
+    for which in range(6):
+        for path in ("spatial", "temporal", "mlp"):
+            m = model_factory(S=S, H=1, d=C, depth=1, temb_dim=4)
+            L = m.layers[0]
+            for k in L:
+                L[k] = np.zeros_like(L[k])
+            if path == "spatial":
+                L["wqkv_s"][:, 2 * C:] = I
+                L["wo_s"] = I.copy()
+            elif path == "temporal":
+                L["wqkv_t"][:, 2 * C:] = I
+                L["wo_t"] = I.copy()
+            else:
+                L["w1"][:, :C] = I
+                L["w2"][:C, :] = I
+            L["wmod"][2, which * C:(which + 1) * C] = a      # temb(0) = [0, 0, 1, 1]
+            got, _, _ = m._layer(L, x, [0] * F, [], ([], []), spatial_self=True)
+            mods = [np.zeros(C)] * 6
+            mods[which] = a
+            lo = {"spatial": 0, "temporal": 2, "mlp": 4}[path]
+            h = ln(x) * (1 + mods[lo + 1]) + mods[lo]
+            if path == "spatial":
+                want = x + h.mean(axis=1, keepdims=True)
+            elif path == "temporal":
+                want = x + np.cumsum(h, axis=0) / np.arange(1, F + 1)[:, None, None]
+            else:
+                want = x + gelu(h)
+            worst = max(worst, float(np.max(np.abs(got - want))))
+    return worst

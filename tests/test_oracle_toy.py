@@ -57,3 +57,124 @@ def test_cached_rollout_equals_full_recompute():
         chunk_of += [ar] * l
         n0 += l
         assert len(cache[0]["tk"]) == min(n0, m.p_max)
+
+
+# ---------------------------------------------------------------------------
+# the block's layer forms, pinned by the mathematics (the pages do not give the
+# backbone, so these are the textbook forms; the GPU toy kernels are checked
+# against exactly these functions)
+# ---------------------------------------------------------------------------
+import math
+
+import pytest
+
+import pins
+from oracle import toy_model
+
+
+def _factory(cls=ToyModel):
+    return lambda **kw: cls(seed=0, **kw)
+
+
+def test_layernorm_pins():
+    assert pins.check_layernorm(toy_model._layernorm) <= 1.0
+
+
+def test_gelu_pins():
+    assert pins.check_gelu_tanh(toy_model._gelu) <= 1.0
+
+
+@pytest.mark.parametrize("temb_dim", [4, 8, 16])
+def test_timestep_embedding_pins(temb_dim):
+    m = ToyModel(seed=0, temb_dim=temb_dim)
+    assert pins.check_timestep_embedding(m.temb, temb_dim // 2) <= 1.0
+
+
+def test_modulation_order_pins():
+    assert pins.check_toy_modulation(_factory(), toy_model._gelu, toy_model._layernorm) <= 1e-12
+
+
+def test_zero_modulation_weights_give_plain_layernorm():
+    # temb(t) @ 0 = 0 for every t: each pre-norm is LN(x) * 1 + 0
+    m = ToyModel(seed=3, temb_dim=8)
+    L = m.layers[0]
+    L["wmod"][:] = 0.0
+    for t in (0, 20, 900):
+        for v in m._mod(L, t):
+            assert np.all(v == 0.0)
+
+
+# planted mistakes in copies of the layer forms: each must fail a pin
+def _ln_no_eps(x):
+    mu = x.mean(-1, keepdims=True)
+    return (x - mu) / np.sqrt(((x - mu) ** 2).mean(-1, keepdims=True))
+
+
+def _ln_sample_var(x):
+    mu = x.mean(-1, keepdims=True)
+    return (x - mu) / np.sqrt(x.var(-1, ddof=1, keepdims=True) + 1e-6)
+
+
+def _ln_no_center(x):
+    return x / np.sqrt(x.var(-1, keepdims=True) + 1e-6)
+
+
+@pytest.mark.parametrize("mutant", [_ln_no_eps, _ln_sample_var, _ln_no_center],
+                         ids=["no_eps", "sample_var", "no_center"])
+def test_layernorm_mutants_fail(mutant):
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = pins.check_layernorm(mutant)
+    assert not (r <= 1.0)
+
+
+def _gelu_c(c, a):
+    return lambda x: 0.5 * x * (1.0 + np.tanh(c * (x + a * x ** 3)))
+
+
+@pytest.mark.parametrize("mutant", [
+    _gelu_c(math.sqrt(math.pi / 2), 0.044715),     # constant inverted
+    _gelu_c(0.7978845608028654, 0.0),              # cubic term dropped
+    _gelu_c(0.7978845608028654, 0.04),             # wrong cubic coefficient
+    _gelu_c(0.8, 0.044715),                        # rounded sqrt(2/pi)
+    lambda x: 0.5 * x * (1.0 - np.tanh(0.7978845608028654 * (x + 0.044715 * x ** 3))),   # sign
+], ids=["inv_const", "no_cubic", "cubic_coef", "rounded_c", "sign"])
+def test_gelu_mutants_fail(mutant):
+    assert pins.check_gelu_tanh(mutant) > 1.0
+
+
+def _temb_mutant(kind, half):
+    def f(t):
+        i = np.arange(half)
+        if kind == "base":
+            w = np.exp(-np.log(10000.0) * i / half)
+        elif kind == "index":
+            w = np.exp(-np.log(1000.0) * (i + 1) / half)
+        else:
+            w = np.exp(-np.log(1000.0) * i / half)
+        a = float(t) * w
+        if kind == "order":
+            return np.concatenate([np.cos(a), np.sin(a)])
+        return np.concatenate([np.sin(a), np.cos(a)])
+    return f
+
+
+@pytest.mark.parametrize("kind", ["base", "index", "order"])
+def test_timestep_embedding_mutants_fail(kind):
+    assert pins.check_timestep_embedding(_temb_mutant(kind, 4), 4) > 1.0
+
+
+class _SwappedShiftScale(ToyModel):
+    def _mod(self, L, t):
+        m = super()._mod(L, t)
+        return [m[1], m[0], m[3], m[2], m[5], m[4]]
+
+
+class _LayerOrderSwapped(ToyModel):
+    def _mod(self, L, t):
+        m = super()._mod(L, t)
+        return [m[2], m[3], m[0], m[1], m[4], m[5]]
+
+
+@pytest.mark.parametrize("cls", [_SwappedShiftScale, _LayerOrderSwapped], ids=["shift_scale", "layer_order"])
+def test_modulation_mutants_fail(cls):
+    assert pins.check_toy_modulation(_factory(cls), toy_model._gelu, toy_model._layernorm) > 1e-6
