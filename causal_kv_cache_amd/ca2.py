@@ -26,7 +26,7 @@ CA2_SPATIAL_PREFIX = 0
 CA2_SPATIAL_SELF = 1
 CA2_STAGE_RING = 1
 CA2_STAGE_SPATIAL = 2
-ABI_VERSION = 2      # include/ca2.h CA2_ABI_VERSION this binding is written for
+ABI_VERSION = 3      # include/ca2.h CA2_ABI_VERSION this binding is written for
 
 _DTYPES = {"f32": CA2_F32, "bf16": CA2_BF16}
 
@@ -43,7 +43,7 @@ class Ca2CacheInfo(ctypes.Structure):
     _fields_ = [("p_k", ctypes.c_int32), ("head_slot", ctypes.c_int32),
                 ("spatial_frames", ctypes.c_int32), ("staged_frames", ctypes.c_int32),
                 ("frames_written", ctypes.c_int64), ("bytes_resident", ctypes.c_uint64),
-                ("ring_slots", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("ring_slots", ctypes.c_int32), ("generation", ctypes.c_uint32)]
 
 
 # name -> (restype, argtypes)
@@ -76,6 +76,7 @@ _SIGS = {
     "ca2_toy_temb_mod": (_I32, [_P, _I32, _P, _I32, _I32, _P, _P]),
     "ca2_toy_ln_mod": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P]),
     "ca2_toy_linear": (_I32, [_P, _I32, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _P]),
+    "ca2_set_spatial_variant": (_I32, [_I32]),
     "ca2_abi_version": (_I32, []),
     "ca2_status_string": (ctypes.c_char_p, [_I32]),
     "ca2_last_error": (ctypes.c_char_p, []),
@@ -149,6 +150,11 @@ def make_config(B, H, d, S, l, p_max, p_spatial, tpe_len, dtype) -> Ca2Config:
 # ----------------------------------------------------------------------------
 # thin functions with the C names
 # ----------------------------------------------------------------------------
+def ca2_set_spatial_variant(variant: int):
+    """Force the bf16 spatial kernel's launch variant (0 = by grid size)."""
+    _check(load().ca2_set_spatial_variant(int(variant)), "ca2_set_spatial_variant")
+
+
 def ca2_tpe_index_raw(first_frame: int, n: int, tpe_len: int):
     lib = load()
     out = (_I32 * max(n, 1))()
@@ -379,7 +385,8 @@ class Cache:
         _check(self._lib.ca2_cache_info_get(self.handle, ctypes.byref(info)), "ca2_cache_info_get")
         return dict(p_k=info.p_k, head_slot=info.head_slot, spatial_frames=info.spatial_frames,
                     staged_frames=info.staged_frames, frames_written=info.frames_written,
-                    bytes_resident=info.bytes_resident, ring_slots=info.ring_slots)
+                    bytes_resident=info.bytes_resident, ring_slots=info.ring_slots,
+                    generation=info.generation)
 
     def ca2_cache_slot_map(self):
         out = (_I32 * self.shape["p_max"])()

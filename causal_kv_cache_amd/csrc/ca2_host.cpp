@@ -32,6 +32,7 @@ struct ca2_cache {
   int32_t ring_slots;    // R: P_max, or P_max + chunk with staging slots
   int32_t staged_n;      // frames written by ca2_qkv_proj_stage, not yet committed
   int32_t staged_targets;
+  uint32_t generation;   // +1 on every state change (write, stage, commit)
   void* ring_k;
   void* ring_v;
   void* sp_k;
@@ -186,6 +187,7 @@ ca2_status create_impl(const ca2_config* cfg, bool staging, ca2_cache** out) {
   c->ring_slots = (int32_t)slots;
   c->staged_n = 0;
   c->staged_targets = 0;
+  c->generation = 0;
   const size_t ring_bytes = (size_t)cfg->batch * c->ring_slots * c->frame_bytes;
   const size_t sp_bytes = (size_t)cfg->batch * cfg->p_spatial * c->frame_bytes;
   // Unwritten slots are filled with 0xFF bytes (a NaN in both dtypes) when
@@ -281,6 +283,7 @@ ca2_status ca2_cache_write(ca2_cache* c, const void* k_t, const void* v_t, const
   hipError_t e = ca2::launch_copy(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "cache_write launch");
   c->frames_written += n;
+  ++c->generation;
   return ok();
 }
 
@@ -393,6 +396,12 @@ ca2_status ca2_spatial_attn_frames(const void* q, const void* k, const void* v, 
   return ok();
 }
 
+ca2_status ca2_set_spatial_variant(int32_t variant) {
+  if (variant < 0 || variant > 4) return fail(CA2_ERR_INVALID_ARG, "variant %d not in [0, 4]", variant);
+  ca2::set_spatial_variant(variant);
+  return ok();
+}
+
 ca2_status ca2_tpe_index_raw(int64_t first, int32_t n, int32_t L, int32_t* out) {
   if (first < 0 || n < 0 || L < 1) return fail(CA2_ERR_INVALID_ARG, "first >= 0, n >= 0, tpe_len >= 1");
   if (n > 0 && !out) return fail(CA2_ERR_INVALID_ARG, "host_out is NULL");
@@ -414,6 +423,7 @@ ca2_status ca2_cache_info_get(const ca2_cache* c, ca2_cache_info* out) {
   out->spatial_frames = (int32_t)(fw < c->cfg.p_spatial ? fw : c->cfg.p_spatial);
   out->staged_frames = c->staged_n;
   out->ring_slots = c->ring_slots;
+  out->generation = c->generation;
   out->frames_written = fw;
   out->bytes_resident = 2ull * c->cfg.batch * (uint64_t)(c->ring_slots + c->cfg.p_spatial) * c->frame_bytes;
   return ok();
@@ -508,8 +518,11 @@ ca2_status ca2_qkv_proj_stage(ca2_cache* c, const void* x, const void* w, const 
                 c_in, c_out);
   const int64_t m = (int64_t)c->cfg.batch * n * c->cfg.tokens;
   if (m > 0x7fffff00 || m * c_in > ((int64_t)1 << 40)) return fail(CA2_ERR_INVALID_ARG, "too large");
-  if ((targets & CA2_STAGE_RING) && c->ring_slots < c->cfg.p_max + n)
-    return fail(CA2_ERR_STATE, "ring staging needs a cache created with ca2_cache_create_staged");
+  // Either target needs staging slots: a commit needs the ring staged, so a
+  // spatial-only staging on a plain cache would overwrite the prefix frames
+  // with no way to commit them.
+  if (c->ring_slots < c->cfg.p_max + n)
+    return fail(CA2_ERR_STATE, "staging needs a cache created with ca2_cache_create_staged");
   if (c->staged_n && (c->staged_n != n || (c->staged_targets & targets)))
     return fail(CA2_ERR_STATE, "already staged: %d frames, targets %d", c->staged_n, c->staged_targets);
   const int64_t fw = c->frames_written;
@@ -540,6 +553,7 @@ ca2_status ca2_qkv_proj_stage(ca2_cache* c, const void* x, const void* w, const 
   if (e != hipSuccess) return hip_fail(e, "qkv_proj_stage launch");
   c->staged_n = n;
   c->staged_targets |= targets;
+  ++c->generation;
   return ok();
 }
 
@@ -553,6 +567,7 @@ ca2_status ca2_cache_commit(ca2_cache* c) {
   c->frames_written += c->staged_n;
   c->staged_n = 0;
   c->staged_targets = 0;
+  ++c->generation;
   return ok();
 }
 

@@ -89,7 +89,12 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
 // explicit vmcnt counts. M0 is a register the compiler reserves, so it warns
 // that the clobber may not be honoured; in the kernels built here every M0
 // reference in the generated code is this one (no indirect register moves,
-// messages or GWS operations), so nothing of the compiler's lives in M0.
+// messages or GWS operations), so nothing of the compiler's lives in M0 --
+// tests/test_m0_guard.py compiles the kernels to assembly and fails if any
+// other instruction writes or reads M0. (The compiler's own builtin for this
+// copy takes a 64-bit per-lane address and makes workgroup-scope release
+// fences wait for every outstanding copy, which would drain the tile
+// pipeline at each barrier.)
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16s(unsigned voff, uint64_t sbase, unsigned lds_addr) {

@@ -115,6 +115,9 @@ hipError_t launch_toy_ln_mod(const float* x, const float* mod, int mod_stride, i
                              int tokens, int rows, int C, float* out, hipStream_t s);
 hipError_t launch_toy_linear(const ToyLinearArgs& a, hipStream_t s);
 
+// Process-wide launch variant of the bf16 spatial kernel (0 = by size, 1..4).
+void set_spatial_variant(int v);
+
 bool temporal_supported(int dtype, int head_dim);
 bool spatial_supported(int dtype, int head_dim);
 

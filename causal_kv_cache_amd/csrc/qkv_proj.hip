@@ -18,7 +18,8 @@
 // 256 rows, each lane's offset from the k-tile base is a constant, and the
 // pad lanes are masked. Within a k-tile the operands of k-step s+1 are read
 // from LDS into a second register set while the 16 MFMAs of k-step s run
-// (one wavefront per SIMD: nothing else would hide the LDS latency).
+// (two wavefronts per SIMD, both of the same workgroup and on the same k-tile
+// schedule, so they hide little of each other's LDS latency).
 // Workgroups are dealt so that each XCD takes a contiguous run of tiles
 // sharing token panels.
 //

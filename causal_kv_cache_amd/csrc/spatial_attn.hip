@@ -32,7 +32,11 @@ namespace {
 // bf16 MFMA kernel: tile geometry and helpers
 // ----------------------------------------------------------------------------
 constexpr int kBN = 64;                  // keys per tile
-constexpr float kNoMax = -1.0e30f;       // running max before the first tile
+// Running max before the first visible key: the most negative finite float,
+// so the first chunk with any finite score raises it (with a larger sentinel,
+// scores below it would never raise the max and the row would end as 0 / 0);
+// exp2 of a masked (-inf) score minus it stays exactly 0.
+constexpr float kNoMax = -__FLT_MAX__;
 constexpr float kLazy = 8.0f;            // raise the running max only past this margin (base 2)
 
 template <int D, int kSW>
@@ -636,6 +640,10 @@ int device_cus() {
   return n;
 }
 
+// Launch variant forced by ca2_set_spatial_variant (a test and measurement
+// switch; 0 = the size-based choice). One relaxed load per launch.
+std::atomic<int> g_forced_variant{0};
+
 template <int D>
 hipError_t launch_mfma(const SpatialArgs& a, hipStream_t s) {
   // Large grids: 4 wavefronts x 64 queries (each K/V operand read from LDS
@@ -649,7 +657,7 @@ hipError_t launch_mfma(const SpatialArgs& a, hipStream_t s) {
   // on copy issue (256-token shape 18.6 -> 17.3 us). With two workgroups per
   // CU, or at d = 64 / 128 (SGPR and VGPR spills under the two-wavefront
   // register cap), it measured slower.
-  // CA2_SPATIAL_CFG=1|2|3|4 forces 32 queries, 64 queries, 8 wavefronts of
+  // Forced variants 1|2|3|4: 32 queries, 64 queries, 8 wavefronts of
   // 32 queries x 2 key halves (two wavefronts per SIMD even at one workgroup
   // per CU; measured slower than 4 x 32 at the 256-token shape, kept
   // selectable), or 32 queries with the copy wavefront.
@@ -657,7 +665,7 @@ hipError_t launch_mfma(const SpatialArgs& a, hipStream_t s) {
   const int64_t wg_big = (int64_t)((a.tokens + 255) / 256) * frames;
   const int64_t wg_small = (int64_t)((a.tokens + 127) / 128) * frames;
   int cfg = wg_big >= 1024 ? 2 : D == 72 && wg_small <= device_cus() ? 4 : 1;
-  if (const char* force = getenv("CA2_SPATIAL_CFG")) cfg = force[0] - '0';
+  if (const int force = g_forced_variant.load(std::memory_order_relaxed)) cfg = force;
   if constexpr (D <= 72) {
     if (cfg == 2) return launch_pipe_cfg<D, 2, 4, 4, 1>(a, s);
   }
@@ -674,6 +682,8 @@ hipError_t launch_f32(const SpatialArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+void set_spatial_variant(int v) { g_forced_variant.store(v, std::memory_order_relaxed); }
 
 bool spatial_supported(int dtype, int d) {
   if (dtype == 0) return d == 16 || d == 32 || d == 64 || d == 72 || d == 128;

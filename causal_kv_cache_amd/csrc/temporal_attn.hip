@@ -324,7 +324,11 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
-constexpr float kNoMax = -1.0e30f;   // running max before any visible key (finite: exp2 gives 0)
+// Running max before any visible key: the most negative finite float, so any
+// finite score raises it on first sight (a larger sentinel would leave scores
+// below it unraised, every P would round to 0 and the row would divide 0 by 0),
+// and exp2 of a masked (-inf) score minus it is still exactly 0.
+constexpr float kNoMax = -__FLT_MAX__;
 constexpr float kLazy = 8.0f;        // raise the running max only past this margin (base 2)
 constexpr int kQPL = 4;              // queries per lane
 

@@ -37,6 +37,15 @@
  *     (queue head, P_k, frames written) is updated when the call is enqueued,
  *     so later calls must be ordered after earlier ones on the device (same
  *     stream, or caller-managed events).
+ *   - HIP graphs: an attention call reads the queue state (head slot, P_k,
+ *     prefix slots) on the host when it is enqueued and passes it to its
+ *     kernel as arguments, so a captured graph keeps the state of the moment
+ *     of capture. Replaying it after a later ca2_cache_write,
+ *     ca2_qkv_proj_stage or ca2_cache_commit on that cache attends over the
+ *     old queue: a captured denoising loop is valid only until the next
+ *     state change. ca2_cache_info.generation changes with every such call,
+ *     so a caller can tell a stale graph (compare it with the value read at
+ *     capture).
  *   - Arguments are validated before anything is launched; on error nothing
  *     is enqueued, the state is unchanged, and ca2_last_error() gives detail.
  *     No call aborts or throws across the ABI.
@@ -97,7 +106,8 @@ typedef struct {
   int64_t frames_written;   /* clean frames ever written (committed) */
   uint64_t bytes_resident;  /* device bytes of ring + spatial buffer */
   int32_t ring_slots;       /* R: physical ring slots (p_max, or p_max + chunk) */
-  int32_t reserved;
+  uint32_t generation;      /* state generation: +1 (mod 2^32) on every ca2_cache_write,
+                               ca2_qkv_proj_stage and ca2_cache_commit that succeeds */
 } ca2_cache_info;
 
 /*
@@ -152,7 +162,9 @@ ca2_status ca2_cache_write(ca2_cache* cache, const void* k_t, const void* v_t,
  * queued frames (oldest first) followed by new frames 0..i; out_i =
  * softmax(scale * q_i . K^T) V over exactly those P_k + i + 1 keys.
  * q, k_new, v_new, out: [B][n][S][H][d] in the cache's dtype.
- * 1 <= n_frames <= chunk; scale > 0 and finite (normally 1/sqrt(d)).
+ * 1 <= n_frames <= chunk; scale > 0 and finite (normally 1/sqrt(d)); the
+ * scaled scores scale * q . k must be finite in float32 (any magnitude up to
+ * that is handled).
  * k_new and v_new may both be NULL when n_frames frames are staged in the
  * ring by ca2_qkv_proj_stage: the new keys/values are then read from their
  * ring slots (the cache-writing pass's attention before the commit).
@@ -171,7 +183,11 @@ ca2_status ca2_temporal_attn(const ca2_cache* cache, const void* q, const void* 
  *   STATE while staged frames in the spatial buffer are not committed.
  * CA2_SPATIAL_SELF: keys/values are the frame's own S tokens (the clean-frame
  *   self-repeat case, whose value equals plain self-attention).
- * q, k, v, out: [B][n][S][H][d]. 1 <= n_frames <= chunk.
+ * q, k, v, out: [B][n][S][H][d]. 1 <= n_frames <= chunk; scale > 0 and
+ * finite. bf16: the scores must satisfy |scale * q . k| < 1e9 (the kernel
+ * evaluates exp2(s c - m) with one fused multiply-add, whose rounding
+ * residue -- a factor common to every P of a row, so it cancels -- stays far
+ * from overflow below that).
  */
 ca2_status ca2_spatial_attn(const ca2_cache* cache, const void* q, const void* k,
                             const void* v, void* out, int32_t n_frames, int32_t mode,
@@ -277,16 +293,18 @@ ca2_status ca2_qkv_proj(const void* x, const void* w, void* q, void* k, void* v,
  *   e_i w^T), or NULL for none;
  * q, k, v: [B][n][S][H][d] bf16 outputs, each may be NULL (not written).
  * targets (ca2_stage_target flags): CA2_STAGE_RING writes K/V into ring
- *   slots (F_w + f) mod R -- needs a cache from ca2_cache_create_staged;
- *   CA2_STAGE_SPATIAL writes the K/V of the last P' frames into the spatial
- *   buffer (frame F at slot F mod P'). The two may come from two calls (two
- *   layers' projections) for the same n.
+ *   slots (F_w + f) mod R; CA2_STAGE_SPATIAL writes the K/V of the last P'
+ *   frames into the spatial buffer (frame F at slot F mod P'). The two may
+ *   come from two calls (two layers' projections) for the same n. Either
+ *   target needs a cache from ca2_cache_create_staged: the commit needs the
+ *   ring staged, so on a plain cache even a spatial-only staging is refused
+ *   (it would overwrite the prefix frames with no way to commit them).
  * The frames stay staged: the queue and the frame count do not move until
  * ca2_cache_commit, so the chunk's temporal attention still sees the queue
  * before eviction (pass k_new = v_new = NULL to read the new frames from the
  * ring). Bf16 caches only; c_in and C multiples of 64, c_in at most 2^20.
  * Errors: INVALID_ARG (NULL x/w, misaligned pointer, bad sizes or targets),
- * STATE (ring target without staging slots; a target already staged, or a
+ * STATE (a cache without staging slots; a target already staged, or a
  * different n, since the last commit), UNSUPPORTED (fp32 cache), HIP.
  */
 ca2_status ca2_qkv_proj_stage(ca2_cache* cache, const void* x, const void* w,
@@ -333,10 +351,21 @@ ca2_status ca2_toy_linear(const float* x, int32_t ldx, const float* w, int32_t l
                           int32_t ldr, float* y, int32_t ldy, int32_t m, int32_t n, int32_t k,
                           int32_t act, void* stream);
 
+/*
+ * Test and measurement switch: force the launch variant of the bf16 spatial
+ * attention kernel for every later call in the process (0 = chosen by grid
+ * size, the default; 1 = 4 wavefronts x 32 queries; 2 = 4 x 64 queries,
+ * head_dim <= 72; 3 = 8 wavefronts, 4 x 32 queries x 2 key halves; 4 = 4 x 32
+ * queries plus a wavefront that issues every tile copy). Every variant
+ * computes the same attention. INVALID_ARG outside [0, 4]. Not synchronised
+ * with calls in flight on other host threads.
+ */
+ca2_status ca2_set_spatial_variant(int32_t variant);
+
 /* Version of this ABI (entry points, argument lists, struct layouts):
  * CA2_ABI_VERSION. A binding compares it with the value it was written for
  * and refuses a library built from other sources. */
-#define CA2_ABI_VERSION 2
+#define CA2_ABI_VERSION 3
 int32_t ca2_abi_version(void);
 
 /* Static description of a status code; any other integer gives

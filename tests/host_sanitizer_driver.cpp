@@ -72,6 +72,11 @@ int main() {
 
   CHECK(ca2_abi_version() == CA2_ABI_VERSION);
 
+  // spatial launch-variant switch: range checked, host state only
+  CHECK(ca2_set_spatial_variant(-1) == CA2_ERR_INVALID_ARG);
+  CHECK(ca2_set_spatial_variant(5) == CA2_ERR_INVALID_ARG);
+  for (int32_t v = 4; v >= 0; --v) CHECK(ca2_set_spatial_variant(v) == CA2_OK);
+
   // status strings
   for (int32_t s = 0; s <= 5; ++s) CHECK(std::strlen(ca2_status_string(s)) > 0);
   CHECK(std::strcmp(ca2_status_string(99), "unknown status") == 0);

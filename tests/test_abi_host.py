@@ -195,3 +195,11 @@ def test_abi_version_matches_header(lib):
     hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ca2.h")).read()
     declared = int(re.search(r"#define CA2_ABI_VERSION (\d+)", hdr).group(1))
     assert lib.load().ca2_abi_version() == declared == lib.ABI_VERSION
+
+
+def test_spatial_variant_switch_range(lib):
+    raw = lib.load()
+    assert raw.ca2_set_spatial_variant(-1) == lib.CA2_ERR_INVALID_ARG
+    assert raw.ca2_set_spatial_variant(5) == lib.CA2_ERR_INVALID_ARG
+    for v in (4, 3, 2, 1, 0):
+        assert raw.ca2_set_spatial_variant(v) == lib.CA2_OK

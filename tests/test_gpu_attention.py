@@ -213,18 +213,21 @@ FULL_TILE_CASES = [
 @pytest.mark.parametrize("name,sh,writes,n,mode",
                          [c for c in SPATIAL_CASES if c[1]["dtype"] == "bf16"] + FULL_TILE_CASES,
                          ids=[c[0] for c in SPATIAL_CASES if c[1]["dtype"] == "bf16"] + [c[0] for c in FULL_TILE_CASES])
-def test_spatial_parity_every_launch_variant(ca2, monkeypatch, cfg, name, sh, writes, n, mode):
+def test_spatial_parity_every_launch_variant(ca2, cfg, name, sh, writes, n, mode):
     """Every bf16 launch variant (4 wavefronts x 32 queries, 4 x 64 queries,
     8 wavefronts = 4 x 32 queries x 2 key halves, 4 x 32 queries plus a
     wavefront that issues every copy) against the oracle, whatever the grid
     size would pick."""
     if cfg == "2" and sh["d"] > 72:
         pytest.skip("64-query wavefronts are built for d <= 72 only")
-    monkeypatch.setenv("CA2_SPATIAL_CFG", cfg)
     cache, o = fill(ca2, sh, 300, writes)
     q, k, v = (o.noisy(x, 2, 4, n) for x in ("q", "k", "v"))
     out = empty_like_dev(q.shape, "bf16")
-    cache.ca2_spatial_attn(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), out, mode=mode)
+    ca2.ca2_set_spatial_variant(int(cfg))
+    try:
+        cache.ca2_spatial_attn(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), out, mode=mode)
+    finally:
+        ca2.ca2_set_spatial_variant(0)
     torch.cuda.synchronize()
     ref = o.spatial_out(q, k, v, "prefix" if mode == 0 else "self")
     check_close(to_host(out), ref, "bf16", f"{name} cfg {cfg}")
@@ -271,3 +274,58 @@ def test_random_configs_both_kernels(ca2, name, sh, writes, n):
                 sh["dtype"], name + " temporal")
     check_close(to_host(out_s), o.spatial_out(q, k, v, "prefix"), sh["dtype"], name + " spatial")
     assert cache.ca2_cache_frame_ids()[0] == o.queue.frame_ids()
+
+
+@pytest.mark.parametrize("kernel,log2a", [("temporal", 52), ("spatial", 11)])
+@pytest.mark.parametrize("pattern", ["uniform", "tiered"])
+def test_large_negative_scores(ca2, pattern, kernel, log2a):
+    """Inputs of magnitude 2^log2a (bf16-exact) with every score negative.
+    Temporal at 2^52: every scaled score is about -1e32 in base 2, far below
+    any finite starting sentinel short of the float range, so the running
+    maximum must be taken from the scores themselves. Spatial at 2^11 (scores
+    about -5e7): the largest magnitude its exp2(fma(s, c, -m)) form supports
+    with margin (the fma's rounding residue is a common factor of every P,
+    which cancels, as long as it cannot overflow: |scaled score| < 2^31).
+    With equal keys the output is the mean of the cached values; with tiered
+    keys it is the mean of the values of the least negative tier (one-hot up
+    to ties at these gaps); either way the oracle's."""
+    from oracle import TemporalQueue, SpatialCache
+    B, H, d, S, l, P, Ps = 1, 2, 72, 64, 8, 8, 3
+    sh = shape_of(B, H, d, S, l, P, Ps, "bf16")
+    a = 2.0 ** log2a
+    g = np.random.default_rng(7)
+    ones = np.ones((B, l, S, H, d), np.float32)
+    tier = np.ones_like(ones)
+    if pattern == "tiered":
+        tier *= (1.0 + (np.arange(l) % 4) / 4.0)[None, :, None, None, None]   # 1, 1.25, 1.5, 1.75
+    k_clean = (-a * tier).astype(np.float32)
+    v_clean = synth.round_to_bf16(g.standard_normal(ones.shape).astype(np.float32))
+    cache = ca2.Cache.from_shape(sh)
+    kd, vd = to_dev(k_clean, "bf16"), to_dev(v_clean, "bf16")
+    cache.ca2_cache_write(kd, vd, kd, vd)
+    q = (a * ones).astype(np.float32)
+    k_new = (-2.0 * a * ones).astype(np.float32)          # below every cached tier
+    v_new = synth.round_to_bf16(g.standard_normal(ones.shape).astype(np.float32))
+    dq, dk, dv = (to_dev(x, "bf16") for x in (q, k_new, v_new))
+    out = empty_like_dev(q.shape, "bf16")
+    if kernel == "temporal":
+        cache.ca2_temporal_attn(dq, dk, dv, out)
+    else:
+        cache.ca2_spatial_attn(dq, dk, dv, out)
+    torch.cuda.synchronize()
+    scale = 1.0 / np.sqrt(d)
+    if kernel == "temporal":
+        tq = TemporalQueue(P)
+        tq.write(range(l))
+        ring_k = np.zeros((B, P, S, H, d), np.float32)
+        ring_v = np.zeros_like(ring_k)
+        ring_k[:, :l], ring_v[:, :l] = k_clean, v_clean
+        ref = temporal_attn_ref(q, k_new, v_new, ring_k, ring_v, tq.slot_map(), scale)
+    else:
+        sc = SpatialCache(Ps)
+        sc.write(range(l))
+        frames = sc.logical_frames()
+        ref = spatial_attn_ref(q, k_new, v_new, k_clean[:, frames], v_clean[:, frames], list(range(Ps)),
+                               scale, "prefix")
+    check_close(to_host(out), ref, "bf16", f"{pattern} {kernel}")
+    cache.close()

@@ -142,3 +142,31 @@ def test_calls_on_a_side_stream_match_the_default_stream(ca2):
         assert torch.equal(a, b)
     for a, b in zip(dumps[0], dumps[1]):
         assert np.array_equal(a, b)
+
+
+def test_generation_counts_state_changes(ca2):
+    """The state generation moves with every write, staging and commit, and
+    with nothing else (attention calls and refused calls leave it alone), so a
+    caller can tell that a captured graph's baked-in queue state is stale."""
+    sh = dict(B=1, H=2, d=64, S=8, l=4, p_max=5, p_spatial=2, tpe_len=9, dtype="bf16")   # H*d multiple of 64
+    B, H, d, S, l = sh["B"], sh["H"], sh["d"], sh["S"], sh["l"]
+    cache = ca2.Cache.from_shape(sh, staged=True)
+    x = torch.zeros((B, l, S, H, d), dtype=torch.bfloat16, device="cuda")
+    gen = [cache.ca2_cache_info_get()["generation"]]
+    cache.ca2_cache_write(x, x, x, x)
+    gen.append(cache.ca2_cache_info_get()["generation"])
+    cache.ca2_temporal_attn(x, x, x, torch.empty_like(x))
+    cache.ca2_spatial_attn(x, x, x, torch.empty_like(x))
+    gen.append(cache.ca2_cache_info_get()["generation"])
+    xs = torch.zeros((B, l, S, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((3 * H * d, 64), dtype=torch.bfloat16, device="cuda")
+    cache.ca2_qkv_proj_stage(xs, w)
+    gen.append(cache.ca2_cache_info_get()["generation"])
+    with pytest.raises(ca2.Ca2Error):
+        cache.ca2_cache_write(x, x, x, x)                    # refused while staged
+    gen.append(cache.ca2_cache_info_get()["generation"])
+    cache.ca2_cache_commit()
+    gen.append(cache.ca2_cache_info_get()["generation"])
+    torch.cuda.synchronize()
+    assert gen == [0, 1, 1, 2, 2, 3]
+    cache.close()

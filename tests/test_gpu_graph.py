@@ -1,48 +1,61 @@
 """HIP-graph capture of the denoising loop (the calls that share one cache
-state between two cache-writing passes).
+state between two cache-writing passes), checked against the oracle.
 
 The loop is captured once and replayed several times, with the program's own
-eager launches and synchronisations between replays; every replay must give
-outputs bit-identical to eager launches of the same calls (the kernels are
-deterministic: no atomics, fixed reduction order).
+eager launches and synchronisations between replays. Every replay's outputs
+are compared element by element with the oracle's prefix spatial and causal
+temporal attention over the same cache state (bf16 bar), and must also be
+bit-identical to eager launches of the same calls (the kernels are
+deterministic: no atomics, fixed reduction order). The cache's state
+generation is read at capture and must be unchanged at every replay (the
+graph's baked-in queue state is current).
 """
 import pytest
 import torch
 
+from oracle import RolloutOracle, temporal_attn_ref
+from gpu_util import to_dev, to_host, check_close
+
 pytestmark = pytest.mark.gpu
 
-SHAPE = dict(B=1, H=16, d=72, S=256, l=8, p_max=25, p_spatial=3, tpe_len=33)
+# the 256-token Ca2-VDM shape of the benchmark step, queue full
+SHAPE = dict(B=1, H=16, d=72, S=256, l=8, p_max=25, p_spatial=3, tpe_len=33, dtype="bf16")
+CALLS = 4
 
 
-def test_denoise_loop_graph_replays_equal_eager(ca2):
+def test_denoise_loop_graph_replays_match_oracle(ca2):
     sh = SHAPE
-    bf = torch.bfloat16
-    cache = ca2.Cache(sh["B"], sh["H"], sh["d"], sh["S"], sh["l"], sh["p_max"], sh["p_spatial"], sh["tpe_len"], "bf16")
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(2024)
-    B, l, S, H, d = sh["B"], sh["l"], sh["S"], sh["H"], sh["d"]
-
-    def randn(n):
-        return torch.randn((B, n, S, H, d), generator=gen, device="cuda", dtype=torch.float32).to(bf)
-
-    frames = 0
-    while frames < sh["p_max"]:                      # queue full, spatial cache full
-        n = 1 if frames == 0 else l
-        cache.ca2_cache_write(randn(n), randn(n), randn(n), randn(n))
-        frames += n
-    T = 10
-    sets = [(randn(l), randn(l), randn(l)) for _ in range(T)]
+    cache = ca2.Cache.from_shape(sh)
+    o = RolloutOracle(sh, 2024)
+    for w in (1, 8, 8, 8):                           # queue and spatial cache full
+        frames = o.next_frames(w)
+        cache.ca2_cache_write(*(to_dev(o.clean(x, frames), "bf16") for x in ("kt", "vt", "ks", "vs")))
+        o.write(frames)
+    n = sh["l"]
+    host = [tuple(o.noisy(x, 1, t, n) for x in ("q", "k", "v")) for t in range(CALLS)]
+    sets = [tuple(to_dev(x, "bf16") for x in qkv) for qkv in host]
     outs = [(torch.empty_like(q), torch.empty_like(q)) for q, _, _ in sets]
+    refs = []
+    for q, k, v in host:
+        refs.append((o.spatial_out(q, k, v, "prefix"),
+                     temporal_attn_ref(q, k, v, o.ring_k, o.ring_v, o.queue.slot_map(), o.scale)))
 
     def loop():
         for (q, k, v), (os_, ot) in zip(sets, outs):
             cache.ca2_spatial_attn(q, k, v, os_)
             cache.ca2_temporal_attn(q, k, v, ot)
 
+    def check_oracle(tag):
+        for i, ((a, b), (rs, rt)) in enumerate(zip(outs, refs)):
+            check_close(to_host(a), rs, "bf16", f"{tag}: spatial call {i}")
+            check_close(to_host(b), rt, "bf16", f"{tag}: temporal call {i}")
+
     loop()
     torch.cuda.synchronize()
-    ref = [(a.clone(), b.clone()) for a, b in outs]
+    check_oracle("eager")
+    eager = [(a.clone(), b.clone()) for a, b in outs]
 
+    gen = cache.ca2_cache_info_get()["generation"]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
@@ -55,12 +68,16 @@ def test_denoise_loop_graph_replays_equal_eager(ca2):
             a.zero_()
             b.zero_()
         torch.cuda.synchronize()
+        assert cache.ca2_cache_info_get()["generation"] == gen
         g.replay()
         torch.cuda.synchronize()
-        for i, ((a, b), (ra, rb)) in enumerate(zip(outs, ref)):
-            assert torch.equal(a, ra), f"replay {rep}: spatial output of call {i} differs from eager"
-            assert torch.equal(b, rb), f"replay {rep}: temporal output of call {i} differs from eager"
+        check_oracle(f"replay {rep}")
+        for i, ((a, b), (ea, eb)) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, ea), f"replay {rep}: spatial output of call {i} differs from eager"
+            assert torch.equal(b, eb), f"replay {rep}: temporal output of call {i} differs from eager"
         loop()                                       # eager work between replays
         torch.cuda.synchronize()
-        for (a, b), (ra, rb) in zip(outs, ref):
-            assert torch.equal(a, ra) and torch.equal(b, rb), "eager launch after a replay differs"
+        for (a, b), (ea, eb) in zip(outs, eager):
+            assert torch.equal(a, ea) and torch.equal(b, eb), "eager launch after a replay differs"
+    del g
+    cache.close()

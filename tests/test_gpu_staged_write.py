@@ -206,10 +206,12 @@ def test_stage_state_errors_leave_the_cache_unchanged(ca2):
     plain = ca2.Cache.from_shape(sh)                         # no staging slots
     plain.ca2_cache_write(q, q, q, q)
     assert status(lambda: plain.ca2_qkv_proj_stage(dx, dw, targets=RING)) == ca2.CA2_ERR_STATE
-    plain.ca2_qkv_proj_stage(dx, dw, targets=SPATIAL)         # the spatial buffer alone is fine
-    assert status(lambda: plain.ca2_spatial_attn(q, q, q, q)) == ca2.CA2_ERR_STATE   # prefix mid-update
-    plain.ca2_spatial_attn(q, q, q, q, mode=ca2.CA2_SPATIAL_SELF)
-    assert status(lambda: plain.ca2_cache_commit()) == ca2.CA2_ERR_STATE           # ring missing
+    # the spatial buffer alone is refused too: the commit needs the ring, so it
+    # would leave the cache with its prefix frames overwritten and no way out
+    assert status(lambda: plain.ca2_qkv_proj_stage(dx, dw, targets=SPATIAL)) == ca2.CA2_ERR_STATE
+    assert plain.ca2_cache_info_get()["staged_frames"] == 0
+    plain.ca2_spatial_attn(q, q, q, q)                        # prefix mode still works
+    assert status(lambda: plain.ca2_cache_commit()) == ca2.CA2_ERR_STATE           # nothing staged
     plain.close()
 
     cache = ca2.Cache.from_shape(sh, staged=True)
