@@ -3,9 +3,10 @@
 A step is one autoregressive step at the 256-token Ca2-VDM shape (B=1, 16
 heads x 72, 16x16 latent tokens, chunk l=8, queue full at P_max=25, P'=3,
 bf16): 50 denoising calls -- each a prefix-enhanced spatial attention and a
-causal temporal attention over the shared cache, with fresh Q/K/V per call --
-then the cache-writing pass: spatial self attention, temporal attention of the
-clean chunk, and the cache write (append + FIFO evict + spatial overwrite).
+causal temporal attention over the shared cache, with fresh Q/K/V per call,
+computed by one fused launch (ca2_denoise_attn) -- then the cache-writing
+pass: spatial self attention, temporal attention of the clean chunk, and the
+cache write (append + FIFO evict + spatial overwrite).
 Inputs are synthetic (seeded N(0,1), bf16) and resident in HBM before timing.
 
 value = denoising-call query tokens (50 * B*l*S per step) / wall time of the
@@ -49,7 +50,8 @@ ROLLOUT = dict(name="rollout_80f", B=1, H=16, d=72, S=256, l=8, p_max=41, p_spat
 ROLLOUT_FRAMES = 80
 ROLLOUT_LAYERS = 8   # attention layers per model call in the rollout comparison
 WORKLOADS = {w["name"]: w for w in (AR_STEP, LARGE, WRITE)}
-KERNELS = ("spatial_prefix", "temporal", "spatial_self", "cache_write", "qkv_proj", "qkv_proj_stage")
+KERNELS = ("spatial_prefix", "temporal", "spatial_self", "cache_write", "qkv_proj", "qkv_proj_stage",
+           "denoise_fused")
 
 
 # ----------------------------------------------------------------------------
@@ -126,6 +128,14 @@ class Workload:
         torch.cuda.synchronize()
 
     def denoise(self, i):
+        """One denoising call: prefix spatial + causal temporal attention over
+        one cache, fused into one launch where the shapes allow it."""
+        q, k, v = self.sets[i % len(self.sets)]
+        c = self.caches[i % len(self.caches)]
+        c.ca2_denoise_attn(q, k, v, self.out_s, q, k, v, self.out_t)
+
+    def denoise_two_launches(self, i):
+        """The same call as two launches (stand-alone spatial, then temporal)."""
         q, k, v = self.sets[i % len(self.sets)]
         c = self.caches[i % len(self.caches)]
         c.ca2_spatial_attn(q, k, v, self.out_s)
@@ -174,7 +184,8 @@ def time_launches(fn, reps, rounds=5):
 
 def denoise_loop_graph(w: Workload, reps: int):
     """The 50 denoising calls of one AR step (they share one state of each
-    cache) launched eagerly and as one captured HIP graph: average ms per loop.
+    cache) launched eagerly as fused calls, eagerly as two launches per call,
+    and as one captured HIP graph of the fused calls: average ms per loop.
     The cache-writing pass changes the queue and cannot be replayed, so the
     headline step launches eagerly; this only reports the difference."""
     import torch
@@ -183,7 +194,12 @@ def denoise_loop_graph(w: Workload, reps: int):
         for t in range(T_DENOISE):
             w.denoise(t)
 
+    def loop2():
+        for t in range(T_DENOISE):
+            w.denoise_two_launches(t)
+
     eager = time_launches(loop, reps) / 1e3
+    two = time_launches(loop2, reps) / 1e3
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
@@ -192,7 +208,7 @@ def denoise_loop_graph(w: Workload, reps: int):
     torch.cuda.synchronize()
     graph = time_launches(g.replay, reps) / 1e3
     del g
-    return eager, graph
+    return eager, two, graph
 
 
 def launchers(w: Workload):
@@ -219,7 +235,12 @@ def launchers(w: Workload):
         qc, kt, vt, ks, vs = w.clean
         c.ca2_spatial_attn(qc, ks, vs, w.out_s, mode=ca2.CA2_SPATIAL_SELF)
 
-    return {"spatial_prefix": k_spatial, "temporal": k_temporal, "spatial_self": k_spatial_self}
+    def k_denoise_fused():
+        c, (q, k, v) = nxt()
+        c.ca2_denoise_attn(q, k, v, w.out_s, q, k, v, w.out_t)
+
+    return {"spatial_prefix": k_spatial, "temporal": k_temporal, "spatial_self": k_spatial_self,
+            "denoise_fused": k_denoise_fused}
 
 
 def main_workload():
@@ -228,8 +249,9 @@ def main_workload():
     return Workload(AR_STEP, T_DENOISE, seed=1234, n_caches=N_CACHES)
 
 
-def kernel_table(w: Workload, reps: int):
-    """Per-kernel average launch duration and roofline numbers for one workload."""
+def kernel_table(w: Workload, reps: int, fused: bool = False):
+    """Per-kernel average launch duration and roofline numbers for one workload
+    (with fused = True also the fused denoising call)."""
     sh = w.sh
     n, pk, ps = sh["l"], sh["p_max"], sh["p_spatial"]
     fns = launchers(w)
@@ -250,12 +272,29 @@ def kernel_table(w: Workload, reps: int):
     rows["spatial_attn_self"] = dict(us=us, us_min=lo, us_max=hi, flops=fl, bytes=spatial_bytes(sh, n, 0),
                                      bound="mfma", achieved=fl / us / 1e6, peak=MFMA_BF16_PEAK_TFLOPS,
                                      unit="TFLOP/s")
+    if fused:
+        # one launch doing both: its roofline is the larger of the two ideal
+        # times of its combined work (bytes at HBM peak, flops at MFMA peak)
+        us, lo, hi = time_launches_stats(fns["denoise_fused"], reps)
+        fl = spatial_flops(sh, n, ps) + temporal_flops(sh, n, pk)
+        by = spatial_bytes(sh, n, ps) + temporal_bytes(sh, n, pk)
+        hbm_bound = by / HBM_PEAK_GBS >= fl / MFMA_BF16_PEAK_TFLOPS / 1e3
+        rows["denoise_fused"] = dict(us=us, us_min=lo, us_max=hi, flops=fl, bytes=by,
+                                     bound="hbm" if hbm_bound else "mfma",
+                                     achieved=by / us / 1e3 if hbm_bound else fl / us / 1e6,
+                                     peak=HBM_PEAK_GBS if hbm_bound else MFMA_BF16_PEAK_TFLOPS,
+                                     unit="GB/s" if hbm_bound else "TFLOP/s",
+                                     mfma_part={"achieved_tflops": round(fl / us / 1e6, 3),
+                                                "frac": round(fl / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)},
+                                     hbm_part={"achieved_gbs": round(by / us / 1e3, 3),
+                                               "frac": round(by / us / 1e3 / HBM_PEAK_GBS, 4)})
     for r in rows.values():
         r["frac"] = r["achieved"] / r["peak"]
     return rows
 
 
 SOURCES = {"spatial_prefix": "spatial_attn.hip", "spatial_self": "spatial_attn.hip",
+           "denoise_fused": "spatial_attn.hip",
            "temporal": "temporal_attn.hip", "cache_write": "cache_write.hip", "qkv_proj": "qkv_proj.hip",
            "qkv_proj_stage": "qkv_proj.hip"}
 
@@ -397,8 +436,7 @@ def rollout_compare():
         for _ in range(T_DENOISE):
             for li in range(L):
                 q, k, v = sets[li]
-                caches[li].ca2_spatial_attn(q, k, v, out_s)
-                caches[li].ca2_temporal_attn(q, k, v, out_t)
+                caches[li].ca2_denoise_attn(q, k, v, out_s, q, k, v, out_t)
 
     def write_all():
         for c in caches:
@@ -575,6 +613,8 @@ def main():
     ap.add_argument("--kernel", choices=KERNELS, help="only launch this kernel (profiling mode)")
     ap.add_argument("--workload", choices=tuple(WORKLOADS), default=AR_STEP["name"])
     ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--spatial-variant", type=int, default=0,
+                    help="profiling mode: force the bf16 spatial launch variant (0 = by size)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -586,6 +626,7 @@ def main():
     ca2.load()
     torch.cuda.set_device(0)
     if args.kernel:
+        ca2.ca2_set_spatial_variant(args.spatial_variant)
         print(json.dumps(kernel_mode(args.kernel, args.workload, args.reps)), flush=True)
         return
 
@@ -605,15 +646,17 @@ def main():
     tokens = args.steps * T_DENOISE * AR_STEP["B"] * AR_STEP["l"] * AR_STEP["S"]
     value = tokens / wall
 
-    loop_eager, loop_graph = denoise_loop_graph(w, 10)
-    kt = kernel_table(w, args.kernel_reps)
-    # dominant kernel of the step: largest total time per step
-    per_step = {"spatial_attn_prefix": T_DENOISE * kt["spatial_attn_prefix"]["us"],
-                "temporal_attn": T_DENOISE * kt["temporal_attn"]["us"],
+    loop_eager, loop_two, loop_graph = denoise_loop_graph(w, 10)
+    kt = kernel_table(w, args.kernel_reps, fused=True)
+    # dominant kernel of the step: largest total time per step (the denoising
+    # calls run as fused launches; the cache-writing pass runs the stand-alone
+    # temporal and self-mode spatial kernels once each)
+    per_step = {"denoise_fused": T_DENOISE * kt["denoise_fused"]["us"],
+                "temporal_attn": kt["temporal_attn"]["us"],
                 "spatial_attn_self": kt["spatial_attn_self"]["us"]}
     dom = max(per_step, key=per_step.get)
     d = kt[dom]
-    kname = {"spatial_attn_prefix": "spatial_prefix", "temporal_attn": "temporal",
+    kname = {"denoise_fused": "denoise_fused", "temporal_attn": "temporal",
              "spatial_attn_self": "spatial_self"}[dom]
     roofline = {"bound": d["bound"], "achieved": round(d["achieved"], 3), "peak": d["peak"],
                 "unit": d["unit"], "frac": round(d["frac"], 4),
@@ -629,7 +672,8 @@ def main():
         "config": {"workload": AR_STEP["name"], "batch": 1, "heads": 16, "head_dim": 72, "tokens": 256,
                    "chunk": 8, "p_max": 25, "p_k": 25, "p_spatial": 3, "denoise_calls_per_step": T_DENOISE},
         "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
-        "denoise_loop_50_calls_ms": {"eager": round(loop_eager, 4), "hip_graph_replay": round(loop_graph, 4)},
+        "denoise_loop_50_calls_ms": {"eager": round(loop_eager, 4), "eager_two_launches_per_call": round(loop_two, 4),
+                                     "hip_graph_replay": round(loop_graph, 4)},
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r.items()}
                     for k, r in kt.items()},

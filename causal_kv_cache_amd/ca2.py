@@ -59,6 +59,8 @@ _SIGS = {
     "ca2_cache_write": (_I32, [_P, _P, _P, _P, _P, _I32, _P]),
     "ca2_temporal_attn": (_I32, [_P, _P, _P, _P, _P, _I32, ctypes.c_float, _P]),
     "ca2_spatial_attn": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, ctypes.c_float, _P]),
+    "ca2_denoise_attn": (_I32, [_P, _P, _P, _P, _P, _I32, ctypes.c_float, _P, _P, _P, _P, ctypes.c_float, _I32,
+                                ctypes.POINTER(_I32), _P]),
     "ca2_tpe_index": (_I32, [_P, _I32, ctypes.POINTER(_I32)]),
     "ca2_tpe_index_raw": (_I32, [_I64, _I32, _I32, ctypes.POINTER(_I32)]),
     "ca2_cache_info_get": (_I32, [_P, ctypes.POINTER(Ca2CacheInfo)]),
@@ -366,6 +368,28 @@ class Cache:
         scale = self.shape["d"] ** -0.5 if scale is None else scale
         _check(self._lib.ca2_temporal_attn(self.handle, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out),
                                            n, scale, _stream(stream)), "ca2_temporal_attn")
+
+    def ca2_denoise_attn(self, q_s, k_s, v_s, out_s, q_t, k_t, v_t, out_t, mode=CA2_SPATIAL_PREFIX,
+                         scale_s=None, scale_t=None, stream=None):
+        """Spatial attention (q_s, k_s, v_s -> out_s) and temporal attention
+        (q_t, k_t, v_t -> out_t; k_t = v_t = None for staged frames) of one
+        denoising call, fused into one launch where the shapes allow it.
+        Returns True when the fused launch ran."""
+        n = q_s.shape[1]
+        for nm, t in (("q_s", q_s), ("k_s", k_s), ("v_s", v_s), ("out_s", out_s), ("q_t", q_t), ("out_t", out_t)):
+            self._chk(nm, t, n)
+        staged = k_t is None and v_t is None
+        if not staged:
+            self._chk("k_t", k_t, n)
+            self._chk("v_t", v_t, n)
+        d = self.shape["d"]
+        scale_s = d ** -0.5 if scale_s is None else scale_s
+        scale_t = d ** -0.5 if scale_t is None else scale_t
+        fused = _I32(0)
+        _check(self._lib.ca2_denoise_attn(self.handle, _ptr(q_s), _ptr(k_s), _ptr(v_s), _ptr(out_s), int(mode),
+                                          scale_s, _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(out_t), scale_t, n,
+                                          ctypes.byref(fused), _stream(stream)), "ca2_denoise_attn")
+        return bool(fused.value)
 
     def ca2_spatial_attn(self, q, k, v, out, mode=CA2_SPATIAL_PREFIX, scale=None, stream=None):
         n = q.shape[1]

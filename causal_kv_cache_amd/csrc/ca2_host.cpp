@@ -287,8 +287,14 @@ ca2_status ca2_cache_write(ca2_cache* c, const void* k_t, const void* v_t, const
   return ok();
 }
 
-ca2_status ca2_temporal_attn(const ca2_cache* c, const void* q, const void* k_new, const void* v_new,
-                             void* out, int32_t n, float scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and kernel arguments of one temporal-attention call over the
+// cache (ca2_temporal_attn, ca2_denoise_attn).
+ca2_status temporal_args(const ca2_cache* c, const void* q, const void* k_new, const void* v_new, void* out,
+                         int32_t n, float scale, ca2::TemporalArgs* a) {
   ca2_status st = check_frames(c, n);
   if (st != CA2_OK) return st;
   // new frames already in the ring: staged by ca2_qkv_proj_stage, not committed
@@ -300,25 +306,24 @@ ca2_status ca2_temporal_attn(const ca2_cache* c, const void* q, const void* k_ne
   st = from_ring ? check_ptrs({q, out}) : check_ptrs({q, k_new, v_new, out});
   if (st != CA2_OK) return st;
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(CA2_ERR_INVALID_ARG, "scale must be finite and > 0");
-  ca2::TemporalArgs a;
-  a.q = q; a.k_new = k_new; a.v_new = v_new; a.out = out;
-  a.ring_k = c->ring_k; a.ring_v = c->ring_v;
-  a.rows_per_batch = c->cfg.tokens * c->cfg.heads;
-  a.rows_total = c->cfg.batch * a.rows_per_batch;
-  a.n = n;
-  a.p_k = queue_len(c);
-  a.head = queue_head(c);
-  a.p_max = c->ring_slots;
-  a.ring_keys = from_ring ? a.p_k + n : a.p_k;
-  a.causal = 1;
-  a.scale_log2e = scale * 1.4426950408889634f;
-  hipError_t e = ca2::launch_temporal(c->cfg.dtype, c->cfg.head_dim, a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "temporal_attn launch");
-  return ok();
+  a->q = q; a->k_new = k_new; a->v_new = v_new; a->out = out;
+  a->ring_k = c->ring_k; a->ring_v = c->ring_v;
+  a->rows_per_batch = c->cfg.tokens * c->cfg.heads;
+  a->rows_total = c->cfg.batch * a->rows_per_batch;
+  a->n = n;
+  a->p_k = queue_len(c);
+  a->head = queue_head(c);
+  a->p_max = c->ring_slots;
+  a->ring_keys = from_ring ? a->p_k + n : a->p_k;
+  a->causal = 1;
+  a->scale_log2e = scale * 1.4426950408889634f;
+  return CA2_OK;
 }
 
-ca2_status ca2_spatial_attn(const ca2_cache* c, const void* q, const void* k, const void* v, void* out,
-                            int32_t n, int32_t mode, float scale, void* stream) {
+// Validation and kernel arguments of one spatial-attention call over the
+// cache (ca2_spatial_attn, ca2_denoise_attn).
+ca2_status spatial_args(const ca2_cache* c, const void* q, const void* k, const void* v, void* out, int32_t n,
+                        int32_t mode, float scale, ca2::SpatialArgs* a) {
   ca2_status st = check_frames(c, n);
   if (st != CA2_OK) return st;
   st = check_ptrs({q, k, v, out});
@@ -326,24 +331,71 @@ ca2_status ca2_spatial_attn(const ca2_cache* c, const void* q, const void* k, co
   if (mode != CA2_SPATIAL_PREFIX && mode != CA2_SPATIAL_SELF) return fail(CA2_ERR_INVALID_ARG, "mode %d", mode);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(CA2_ERR_INVALID_ARG, "scale must be finite and > 0");
   const int32_t Ps = c->cfg.p_spatial;
-  ca2::SpatialArgs a;
-  memset(&a, 0, sizeof(a));
-  a.q = q; a.k = k; a.v = v; a.out = out;
-  a.sp_k = c->sp_k; a.sp_v = c->sp_v;
-  a.batch = c->cfg.batch; a.n = n; a.tokens = c->cfg.tokens; a.heads = c->cfg.heads;
-  a.p_slots = Ps;
-  a.n_prefix = 0;
+  memset(a, 0, sizeof(*a));
+  a->q = q; a->k = k; a->v = v; a->out = out;
+  a->sp_k = c->sp_k; a->sp_v = c->sp_v;
+  a->batch = c->cfg.batch; a->n = n; a->tokens = c->cfg.tokens; a->heads = c->cfg.heads;
+  a->p_slots = Ps;
+  a->n_prefix = 0;
   if (mode == CA2_SPATIAL_PREFIX && Ps > 0) {
     if (c->frames_written < 1)
       return fail(CA2_ERR_STATE, "prefix mode needs at least one clean frame in the cache");
     if (c->staged_targets & CA2_STAGE_SPATIAL)
       return fail(CA2_ERR_STATE, "prefix mode while the spatial buffer holds staged, uncommitted frames");
-    a.n_prefix = Ps;
-    for (int32_t j = 0; j < Ps; ++j) a.prefix_slot[j] = (int32_t)(spatial_frame(c->frames_written, Ps, j) % Ps);
+    a->n_prefix = Ps;
+    for (int32_t j = 0; j < Ps; ++j) a->prefix_slot[j] = (int32_t)(spatial_frame(c->frames_written, Ps, j) % Ps);
   }
-  a.scale_log2e = scale * 1.4426950408889634f;
+  a->scale_log2e = scale * 1.4426950408889634f;
+  return CA2_OK;
+}
+
+bool overlap(const void* a, const void* b, size_t bytes) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + bytes && y < x + bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+ca2_status ca2_temporal_attn(const ca2_cache* c, const void* q, const void* k_new, const void* v_new,
+                             void* out, int32_t n, float scale, void* stream) {
+  ca2::TemporalArgs a;
+  ca2_status st = temporal_args(c, q, k_new, v_new, out, n, scale, &a);
+  if (st != CA2_OK) return st;
+  hipError_t e = ca2::launch_temporal(c->cfg.dtype, c->cfg.head_dim, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "temporal_attn launch");
+  return ok();
+}
+
+ca2_status ca2_spatial_attn(const ca2_cache* c, const void* q, const void* k, const void* v, void* out,
+                            int32_t n, int32_t mode, float scale, void* stream) {
+  ca2::SpatialArgs a;
+  ca2_status st = spatial_args(c, q, k, v, out, n, mode, scale, &a);
+  if (st != CA2_OK) return st;
   hipError_t e = ca2::launch_spatial(c->cfg.dtype, c->cfg.head_dim, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "spatial_attn launch");
+  return ok();
+}
+
+ca2_status ca2_denoise_attn(const ca2_cache* c, const void* q_s, const void* k_s, const void* v_s, void* out_s,
+                            int32_t mode, float scale_s, const void* q_t, const void* k_t, const void* v_t,
+                            void* out_t, float scale_t, int32_t n, int32_t* fused, void* stream) {
+  ca2::SpatialArgs sa;
+  ca2::TemporalArgs ta;
+  ca2_status st = spatial_args(c, q_s, k_s, v_s, out_s, n, mode, scale_s, &sa);
+  if (st != CA2_OK) return st;
+  st = temporal_args(c, q_t, k_t, v_t, out_t, n, scale_t, &ta);
+  if (st != CA2_OK) return st;
+  const size_t bytes = (size_t)c->cfg.batch * n * c->frame_bytes;
+  if (overlap(out_s, out_t, bytes)) return fail(CA2_ERR_INVALID_ARG, "out_s and out_t overlap");
+  for (const void* in : {q_s, k_s, v_s, q_t, k_t, v_t})
+    if (in && (overlap(in, out_s, bytes) || overlap(in, out_t, bytes)))
+      return fail(CA2_ERR_INVALID_ARG, "an input overlaps an output");
+  bool f = false;
+  hipError_t e = ca2::launch_denoise_call(c->cfg.dtype, c->cfg.head_dim, sa, ta, static_cast<hipStream_t>(stream), &f);
+  if (e != hipSuccess) return hip_fail(e, "denoise_attn launch");
+  if (fused) *fused = f ? 1 : 0;
   return ok();
 }
 

@@ -115,6 +115,16 @@ hipError_t launch_toy_ln_mod(const float* x, const float* mod, int mod_stride, i
                              int tokens, int rows, int C, float* out, hipStream_t s);
 hipError_t launch_toy_linear(const ToyLinearArgs& a, hipStream_t s);
 
+// One denoising call's two attention layers, on independent tensors: the
+// spatial attention `sa` and the temporal attention `ta`. One fused launch
+// where denoise_call_fusable() holds (bf16, head_dim 64 or 72, whole 64-token
+// tiles, causal, n <= 8, the spatial grid within one round of workgroups, no
+// forced spatial variant); otherwise the two kernels back to back on `s`.
+// *fused (if not NULL) tells which.
+bool denoise_call_fusable(int dtype, int head_dim, const SpatialArgs& sa, const TemporalArgs& ta);
+hipError_t launch_denoise_call(int dtype, int head_dim, const SpatialArgs& sa, const TemporalArgs& ta, hipStream_t s,
+                               bool* fused);
+
 // Process-wide launch variant of the bf16 spatial kernel (0 = by size, 1..4).
 void set_spatial_variant(int v);
 

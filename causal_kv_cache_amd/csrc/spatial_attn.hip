@@ -21,6 +21,7 @@
 // The fp32 path (for fp32 caches) is a plain LDS-tiled VALU kernel.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "temporal_common.hpp"
 
 #include <atomic>
 #include <cstdlib>
@@ -32,12 +33,9 @@ namespace {
 // bf16 MFMA kernel: tile geometry and helpers
 // ----------------------------------------------------------------------------
 constexpr int kBN = 64;                  // keys per tile
-// Running max before the first visible key: the most negative finite float,
-// so the first chunk with any finite score raises it (with a larger sentinel,
-// scores below it would never raise the max and the row would end as 0 / 0);
-// exp2 of a masked (-inf) score minus it stays exactly 0.
-constexpr float kNoMax = -__FLT_MAX__;
-constexpr float kLazy = 8.0f;            // raise the running max only past this margin (base 2)
+// The running maximum starts at kNoMax (the most negative finite float, so
+// any finite score raises it) and is raised lazily, only past kLazy (base 2);
+// both constants come with the temporal helpers.
 
 template <int D, int kSW>
 struct SCfg {
@@ -137,10 +135,12 @@ __device__ __forceinline__ void lazy_rescale(float mx_raw, float c, float& m_run
 // iteration t a wavefront waits for its copies of tile t+1 and, after the
 // barrier, refills the stage of tile t-1 with tile t+kStages-1.
 
+// The body, for the kSW (+ PROD) wavefronts of a workgroup with thread
+// index tid < 64 * (kSW + PROD), work item w (frame-head-query block) and the
+// ring `smem` (kStages * STAGE bytes of LDS). Every wavefront that runs it
+// takes exactly n_tiles workgroup barriers.
 template <int D, int QB, int kSW, bool FULL, int kStages, int KS, bool PROD>
-// (d > 72: the ring of one workgroup takes most of the CU's LDS, so one
-// wavefront per SIMD is all that can be resident)
-__global__ __launch_bounds__(64 * (kSW + PROD)) __attribute__((amdgpu_waves_per_eu(D <= 72 ? 2 : 1, 8))) void spatial_attn_pipe_kernel(SpatialArgs a) {
+__device__ __forceinline__ void spatial_pipe(const SpatialArgs& a, int w, int tid, unsigned char* smem) {
   using C = SCfg<D, PROD ? 1 : kSW>;
   static_assert(KS == 1 || KS == 2, "key split over one or two wavefronts");
   static_assert(!PROD || KS == 1, "a copy wavefront only with one key range per wavefront");
@@ -149,9 +149,6 @@ __global__ __launch_bounds__(64 * (kSW + PROD)) __attribute__((amdgpu_waves_per_
   static_assert(kStages >= 3, "the pipeline reads tile t+1 while tile t+2 is copied");
   constexpr int KSTEPS = C::KSTEPS, DBLK = C::DBLK, KSL = C::KSL, VSL = C::VSL, CH = C::CH;
   constexpr int MAXI = C::MAXI;                    // copies per wavefront per tile (upper bound)
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * C::STAGE];
-
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // PROD: wavefront kSW issues every copy and computes nothing
@@ -162,7 +159,6 @@ __global__ __launch_bounds__(64 * (kSW + PROD)) __attribute__((amdgpu_waves_per_
   const int col = lane & 31;
   const int S = a.tokens;
   const int nq = (S + 32 * QB * G - 1) / (32 * QB * G);
-  const int w = xcd_work_index(blockIdx.x, gridDim.x);
   const int qblk = w % nq;
   const int f = (w / nq) % a.n;
   const int head = (w / (nq * a.n)) % a.heads;
@@ -543,6 +539,229 @@ __global__ __launch_bounds__(64 * (kSW + PROD)) __attribute__((amdgpu_waves_per_
   }
 }
 
+template <int D, int QB, int kSW, bool FULL, int kStages, int KS, bool PROD>
+// (d > 72: the ring of one workgroup takes most of the CU's LDS, so one
+// wavefront per SIMD is all that can be resident)
+__global__ __launch_bounds__(64 * (kSW + PROD)) __attribute__((amdgpu_waves_per_eu(D <= 72 ? 2 : 1, 8))) void spatial_attn_pipe_kernel(SpatialArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * SCfg<D, PROD ? 1 : kSW>::STAGE];
+  spatial_pipe<D, QB, kSW, FULL, kStages, KS, PROD>(a, xcd_work_index(blockIdx.x, gridDim.x), threadIdx.x, smem);
+}
+
+// ----------------------------------------------------------------------------
+// One denoising call in one launch: prefix spatial attention of the chunk
+// (MFMA-bound) and causal temporal attention over the queue (HBM-bound)
+// ----------------------------------------------------------------------------
+// A workgroup holds the four compute wavefronts of one spatial work item
+// (4 x 32 queries, each issuing its share of the tile copies) and kDcTW
+// temporal wavefronts that serve a block of temporal rows, so every SIMD runs
+// one MFMA-and-softmax wavefront beside one wavefront that mostly waits for
+// HBM. The workgroup barriers of the spatial tile ring count every wavefront
+// of the workgroup, so the temporal wavefronts take the same number of
+// barriers, one after each key pair they process: their work advances one
+// key pair per spatial tile, with loads two pairs ahead in a register ring,
+// and whatever is left after the spatial loop's last barrier runs free.
+// Rows of a temporal wavefront: 4 dimension groups x kDcQH query groups of
+// kDcQPL queries, so a row's 8 new frames are covered and 4 rows share a
+// wavefront; the key range is not split, so no partial results are merged.
+constexpr int kDcQH = 4;                         // query groups per temporal row
+constexpr int kDcQPL = 2;                        // queries per lane
+constexpr int kDcTW = 4;                         // temporal wavefronts per workgroup
+constexpr int kDcRows = 64 / (4 * kDcQH);        // rows per temporal wavefront
+constexpr int kDcBlockRows = kDcTW * kDcRows;    // rows per row block of a workgroup
+#ifndef CA2_DC_RING
+#define CA2_DC_RING 6
+#endif
+constexpr int kDcRing = CA2_DC_RING;             // keys in flight per temporal lane
+
+// A wavefront-uniform barrier for wavefronts that share nothing through LDS
+// (they only keep count with the spatial wavefronts' barriers).
+__device__ __forceinline__ void count_barrier(int& bars) {
+  if (bars > 0) {
+    __builtin_amdgcn_s_barrier();
+    --bars;
+  }
+}
+
+// Temporal wavefront tw of a workgroup: row blocks blk0 .. blk0 + nblk - 1
+// (kDcBlockRows rows each), taking exactly `bars` workgroup barriers.
+template <int D, int kPF>
+__device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw, int blk0, int nblk, int bars) {
+  static_assert(kPF % 2 == 0 && kPF >= 4, "register ring of whole key pairs");
+  using G = DsGeom<D>;
+  constexpr int DW = G::DW, DPL = G::DPL, QPL = kDcQPL, QH = kDcQH, LPR = 4 * QH;
+  const int lane = threadIdx.x & 63;
+  const int g = lane & 3;                          // dimension group
+  const int qg = (lane >> 2) % QH;                 // query group
+  const int ri = lane / LPR;
+  const int rpb = a.rows_per_batch;
+  const int64_t frame_bytes = (int64_t)rpb * D * 2;
+  const unsigned char* qb = static_cast<const unsigned char*>(a.q);
+  const unsigned char* knb = static_cast<const unsigned char*>(a.k_new);
+  const unsigned char* vnb = static_cast<const unsigned char*>(a.v_new);
+  const unsigned char* rkb = static_cast<const unsigned char*>(a.ring_k);
+  const unsigned char* rvb = static_cast<const unsigned char*>(a.ring_v);
+  unsigned char* ob = static_cast<unsigned char*>(a.out);
+  const int k_total = a.p_k + a.n;
+  // every query of the row is served here (n <= QPL * QH), so the keys are
+  // all k_total of them; query i stops at key p_k + i (causal)
+  const int ke = k_total;
+  bool first = true;
+
+  for (int blk = blk0; blk < blk0 + nblk; ++blk) {
+    const int row = (blk * kDcTW + tw) * kDcRows + ri;
+    const bool row_ok = row < a.rows_total;
+    const int b = row_ok ? row / rpb : 0;
+    const int rr = row_ok ? row % rpb : 0;
+    const int64_t row_bytes = (int64_t)rr * D * 2;
+    Slice<D> qs[QPL];
+    bool qok[QPL];
+    int last_key[QPL];
+    // every load is unconditional, indices clamped into range (as in the
+    // stand-alone temporal kernel: the compiler's wait counts then keep the
+    // refills in flight across iterations); clamped reads are masked
+#pragma unroll
+    for (int qq = 0; qq < QPL; ++qq) {
+      const int qi = qg * QPL + qq;
+      qok[qq] = row_ok && qi < a.n;
+      last_key[qq] = !qok[qq] ? -1 : a.causal ? a.p_k + qi : k_total - 1;
+      load_slice<D>(qs[qq], qb + ((int64_t)b * a.n + min(qi, a.n - 1)) * frame_bytes + row_bytes, g);
+    }
+    auto key_row = [&](int j, const unsigned char* ring, const unsigned char* fresh) -> const unsigned char* {
+      if (j < a.ring_keys) {
+        int slot = a.head + j;
+        if (slot >= a.p_max) slot -= a.p_max;
+        return ring + ((int64_t)b * a.p_max + slot) * frame_bytes + row_bytes;
+      }
+      return fresh + ((int64_t)b * a.n + (j - a.p_k)) * frame_bytes + row_bytes;
+    };
+    float m[QPL], l[QPL], acc[QPL][DPL];
+#pragma unroll
+    for (int qq = 0; qq < QPL; ++qq) {
+      m[qq] = kNoMax;
+      l[qq] = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[qq][e] = 0.f;
+    }
+    Slice<D> kr[kPF], vr[kPF];
+    auto refill = [&](int u, int jn) {
+      const int jc = jn < ke ? jn : ke - 1;
+      load_slice<D>(kr[u], key_row(jc, rkb, knb), g);
+      load_slice<D>(vr[u], key_row(jc, rvb, vnb), g);
+    };
+#pragma unroll
+    for (int u = 0; u < kPF; ++u) refill(u, u);
+    if (first) {           // the first barrier once the first keys are in flight
+      count_barrier(bars);
+      first = false;
+    }
+    // one key pair: scores, lazy rescale, P rounded to bf16, O += P V by bf16
+    // dot products over the two keys (as the stand-alone temporal kernel)
+    auto process2 = [&](int j, const Slice<D>& k0, const Slice<D>& v0, const Slice<D>& k1, const Slice<D>& v1,
+                        bool two) {
+      float x0[QPL], x1[QPL];
+      bool raise = false;
+#pragma unroll
+      for (int qq = 0; qq < QPL; ++qq) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int x = 0; x < DW; ++x) {
+          s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, qs[qq].w[x]),
+                                               __builtin_bit_cast(bf16x2v, k0.w[x]), s0, false);
+          s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, qs[qq].w[x]),
+                                               __builtin_bit_cast(bf16x2v, k1.w[x]), s1, false);
+        }
+        s0 = quad_sum(s0);
+        s1 = quad_sum(s1);
+        x0[qq] = (j <= last_key[qq]) ? s0 * a.scale_log2e : -INFINITY;
+        x1[qq] = (two && j + 1 <= last_key[qq]) ? s1 * a.scale_log2e : -INFINITY;
+        raise |= fmaxf(x0[qq], x1[qq]) > m[qq] + kLazy;
+      }
+      if (raise) {
+#pragma unroll
+        for (int qq = 0; qq < QPL; ++qq) {
+          const float mn = fmaxf(m[qq], fmaxf(x0[qq], x1[qq]));
+          const float corr = fast_exp2(m[qq] - mn);
+          m[qq] = mn;
+          l[qq] *= corr;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[qq][e] *= corr;
+        }
+      }
+      uint32_t vp[DPL];
+#pragma unroll
+      for (int x = 0; x < DW; ++x) {
+        const uint32_t hi = two ? v1.w[x] : 0u;
+        vp[2 * x] = __builtin_amdgcn_perm(hi, v0.w[x], 0x05040100u);       // low halves
+        vp[2 * x + 1] = __builtin_amdgcn_perm(hi, v0.w[x], 0x07060302u);   // high halves
+      }
+#pragma unroll
+      for (int qq = 0; qq < QPL; ++qq) {
+        const bf16x2v pp = __builtin_bit_cast(bf16x2v, pack_bf16x2(fast_exp2(x0[qq] - m[qq]),
+                                                                   fast_exp2(x1[qq] - m[qq])));
+        l[qq] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2v, 0x3F803F80u), l[qq], false);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+          acc[qq][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2v, vp[e]), acc[qq][e], false);
+      }
+    };
+    for (int j = 0; j < ke; j += kPF) {              // bounds are uniform per wavefront
+#pragma unroll
+      for (int u = 0; u < kPF; u += 2) {             // ring slots are compile-time constants
+        process2(j + u, kr[u], vr[u], kr[u + 1], vr[u + 1], j + u + 1 < ke);   // masked past ke
+        refill(u, j + u + kPF);
+        refill(u + 1, j + u + 1 + kPF);
+        count_barrier(bars);
+      }
+    }
+#pragma unroll
+    for (int qq = 0; qq < QPL; ++qq) {
+      if (!qok[qq]) continue;
+      const int qi = qg * QPL + qq;
+      const float inv = 1.f / l[qq];
+      float o[DPL];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = acc[qq][e] * inv;
+      store_slice<D>(ob + ((int64_t)b * a.n + qi) * frame_bytes + row_bytes, g, o);
+    }
+  }
+  if (first) count_barrier(bars);
+  while (bars > 0) count_barrier(bars);          // the rest of the spatial wavefronts' barriers
+}
+
+// Wavefronts 0..3: spatial work item w (4 x 32 queries, whole 64-key tiles,
+// copies issued by the computing wavefronts); wavefronts 4..4+kDcTW-1:
+// temporal row blocks [blockIdx.x * nblk, +nblk). Launched only when the
+// spatial grid fits on the chip in one round (one workgroup per CU).
+template <int D, int kStages, int kPF>
+__global__ __launch_bounds__(64 * (4 + kDcTW)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void denoise_call_kernel(SpatialArgs sa, TemporalArgs ta, int nblk) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * SCfg<D, 4>::STAGE];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave < 4) {
+    spatial_pipe<D, 1, 4, true, kStages, 1, false>(sa, xcd_work_index(blockIdx.x, gridDim.x), threadIdx.x, smem);
+  } else {
+    const int n_tiles = (1 + sa.n_prefix) * (sa.tokens / kBN);   // the spatial wavefronts' barrier count
+    temporal_lockstep<D, kPF>(ta, wave - 4, blockIdx.x * nblk, nblk, n_tiles);
+  }
+}
+
+// The same two halves in separate workgroups of one launch: blocks
+// [0, n_spatial) are spatial work items (4 computing wavefronts), blocks
+// [n_spatial, 2 n_spatial) temporal row blocks (kDcTW wavefronts, nblk row
+// blocks each). Both kinds fit on a CU together, and nothing couples their
+// progress.
+template <int D, int kStages, int kPF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void denoise_split_kernel(SpatialArgs sa, TemporalArgs ta, int n_spatial, int nblk) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * SCfg<D, 4>::STAGE];
+  if ((int)blockIdx.x < n_spatial) {
+    spatial_pipe<D, 1, 4, true, kStages, 1, false>(sa, xcd_work_index(blockIdx.x, n_spatial), threadIdx.x, smem);
+  } else {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    temporal_lockstep<D, kPF>(ta, wave, ((int)blockIdx.x - n_spatial) * nblk, nblk, 0);
+  }
+}
+
 // ----------------------------------------------------------------------------
 // fp32 kernel: one lane per query, K/V tiles of 32 keys in LDS
 // ----------------------------------------------------------------------------
@@ -684,6 +903,42 @@ hipError_t launch_f32(const SpatialArgs& a, hipStream_t s) {
 }  // namespace
 
 void set_spatial_variant(int v) { g_forced_variant.store(v, std::memory_order_relaxed); }
+
+bool denoise_call_fusable(int dtype, int d, const SpatialArgs& sa, const TemporalArgs& ta) {
+  if (dtype != 1 || (d != 64 && d != 72)) return false;                // the bf16 MFMA path, 2 waves per SIMD
+  if (sa.tokens % kBN != 0 || ta.n > kDcQH * kDcQPL || !ta.causal) return false;
+  if (g_forced_variant.load(std::memory_order_relaxed) != 0) return false;   // a forced spatial variant wins
+  const int64_t nwg = (int64_t)((sa.tokens + 127) / 128) * sa.n * sa.heads * sa.batch;
+  return nwg <= device_cus();                                          // one round of workgroups
+}
+
+hipError_t launch_denoise_call(int dtype, int d, const SpatialArgs& sa, const TemporalArgs& ta, hipStream_t s,
+                               bool* fused) {
+  const bool f = denoise_call_fusable(dtype, d, sa, ta);
+  if (fused) *fused = f;
+  if (!f) {
+    hipError_t e = launch_spatial(dtype, d, sa, s);
+    if (e != hipSuccess) return e;
+    return launch_temporal(dtype, d, ta, s);
+  }
+  // same ring-key rule as the stand-alone temporal launch
+  if (ta.n < 1 || ta.p_k < 0) return hipErrorInvalidValue;
+  if (ta.ring_keys != ta.p_k && ta.ring_keys != ta.p_k + ta.n) return hipErrorInvalidValue;
+  if (ta.ring_keys > 0 && (ta.head < 0 || ta.head >= ta.p_max || ta.ring_keys > ta.p_max)) return hipErrorInvalidValue;
+  const int64_t nwg = (int64_t)((sa.tokens + 127) / 128) * sa.n * sa.heads * sa.batch;
+  const int64_t blocks = ((int64_t)ta.rows_total + kDcBlockRows - 1) / kDcBlockRows;
+  const int nblk = (int)((blocks + nwg - 1) / nwg);
+#ifdef CA2_DC_SPLIT
+  const dim3 grid((unsigned)(2 * nwg)), block(256);
+  if (d == 64) hipLaunchKernelGGL((denoise_split_kernel<64, 4, kDcRing>), grid, block, 0, s, sa, ta, (int)nwg, nblk);
+  else hipLaunchKernelGGL((denoise_split_kernel<72, 4, kDcRing>), grid, block, 0, s, sa, ta, (int)nwg, nblk);
+#else
+  const dim3 grid((unsigned)nwg), block(64 * (4 + kDcTW));
+  if (d == 64) hipLaunchKernelGGL((denoise_call_kernel<64, 4, kDcRing>), grid, block, 0, s, sa, ta, nblk);
+  else hipLaunchKernelGGL((denoise_call_kernel<72, 4, kDcRing>), grid, block, 0, s, sa, ta, nblk);
+#endif
+  return hipGetLastError();
+}
 
 bool spatial_supported(int dtype, int d) {
   if (dtype == 0) return d == 16 || d == 32 || d == 64 || d == 72 || d == 128;

@@ -194,6 +194,31 @@ ca2_status ca2_spatial_attn(const ca2_cache* cache, const void* q, const void* k
                             float scale, void* stream);
 
 /*
+ * Both attention layers of one denoising call over the shared cache, in one
+ * launch where the shapes allow it ([notes] overall framework: every
+ * denoising step runs the model over the noisy chunk against the same
+ * cache; key design 3 for the spatial layer, key designs 1 and 4 for the
+ * temporal layer). Computes exactly what
+ *   ca2_spatial_attn(cache, q_s, k_s, v_s, out_s, n, mode, scale_s) and
+ *   ca2_temporal_attn(cache, q_t, k_t, v_t, out_t, n, scale_t)
+ * compute on the same cache state, with the same arguments, layouts and
+ * errors (k_t = v_t = NULL reads staged frames from the ring). The two must
+ * be independent: no input may overlap an output, nor out_s overlap out_t
+ * (INVALID_ARG). The spatial work is MFMA-bound and the temporal work
+ * HBM-bound, so one workgroup runs both: its four spatial wavefronts and four
+ * temporal wavefronts share every SIMD.
+ * Fused when: bf16 cache, head_dim 64 or 72, tokens a multiple of 64,
+ * n_frames <= 8, the spatial work fits the chip's compute units in one round
+ * (ceil(tokens/128) * n * heads * batch workgroups), and no spatial launch
+ * variant is forced (ca2_set_spatial_variant). Otherwise the two kernels
+ * run back to back on `stream`. *fused (may be NULL) is set to 1 or 0.
+ */
+ca2_status ca2_denoise_attn(const ca2_cache* cache, const void* q_s, const void* k_s, const void* v_s,
+                            void* out_s, int32_t mode, float scale_s, const void* q_t, const void* k_t,
+                            const void* v_t, void* out_t, float scale_t, int32_t n_frames, int32_t* fused,
+                            void* stream);
+
+/*
  * Cache-less temporal attention over T frames, [B][T][S][H][d] tensors in
  * `dtype` (ca2_dtype): for each row (b, s, h) and frame t, out_t =
  * softmax(scale * q_t . K^T) V over keys 0..t (causal = 1: full causal

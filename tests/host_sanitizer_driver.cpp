@@ -72,6 +72,10 @@ int main() {
 
   CHECK(ca2_abi_version() == CA2_ABI_VERSION);
 
+  // the fused denoising call validates like its two halves
+  CHECK(ca2_denoise_attn(nullptr, nullptr, nullptr, nullptr, nullptr, 0, 1.f, nullptr, nullptr, nullptr,
+                         nullptr, 1.f, 1, nullptr, nullptr) == CA2_ERR_INVALID_ARG);
+
   // spatial launch-variant switch: range checked, host state only
   CHECK(ca2_set_spatial_variant(-1) == CA2_ERR_INVALID_ARG);
   CHECK(ca2_set_spatial_variant(5) == CA2_ERR_INVALID_ARG);
