@@ -147,8 +147,8 @@ class Workload:
         c = self.caches[self.passes % len(self.caches)]
         self.passes += 1
         c.ca2_tpe_index(self.sh["l"])
-        c.ca2_temporal_attn(qc, kt, vt, self.out_t)
-        c.ca2_spatial_attn(qc, ks, vs, self.out_s, mode=ca2.CA2_SPATIAL_SELF)
+        # the pass's spatial (self mode) and temporal attention in one launch
+        c.ca2_denoise_attn(qc, ks, vs, self.out_s, qc, kt, vt, self.out_t, mode=ca2.CA2_SPATIAL_SELF)
         c.ca2_cache_write(kt, vt, ks, vs)
 
     def ar_step(self):
@@ -440,8 +440,7 @@ def rollout_compare():
 
     def write_all():
         for c in caches:
-            c.ca2_temporal_attn(qc, kt, vt, out_t)
-            c.ca2_spatial_attn(qc, ks, vs, out_s, mode=ca2.CA2_SPATIAL_SELF)
+            c.ca2_denoise_attn(qc, ks, vs, out_s, qc, kt, vt, out_t, mode=ca2.CA2_SPATIAL_SELF)
             c.ca2_cache_write(kt, vt, ks, vs)
 
     steps = []

@@ -558,8 +558,16 @@ __global__ __launch_bounds__(64 * (kSW + PROD)) __attribute__((amdgpu_waves_per_
 // HBM. The workgroup barriers of the spatial tile ring count every wavefront
 // of the workgroup, so the temporal wavefronts take the same number of
 // barriers, one after each key pair they process: their work advances one
-// key pair per spatial tile, with loads two pairs ahead in a register ring,
-// and whatever is left after the spatial loop's last barrier runs free.
+// key pair per spatial tile, with loads kDcRing keys ahead in a register
+// ring, and whatever is left after the spatial loop's last barrier runs free.
+// Measured alternatives, all within 3 % of this form at the 256-token shape
+// (27-28 us per call against 16.8 + 14.5 us for the two kernels alone):
+// the temporal keys staged through LDS by the same copies as the spatial
+// tiles (4 copies per key pair instead of 12 lane-duplicated loads, 140
+// VGPRs), the same plus the spatial copy wavefront (9 wavefronts), and the
+// two halves as separate workgroups of one launch with no shared barriers.
+// Timing-only copies isolate the cost: the temporal loads alone add ~3.6 us
+// to the spatial half, its arithmetic alone ~2.8 us, both together ~9 us.
 // Rows of a temporal wavefront: 4 dimension groups x kDcQH query groups of
 // kDcQPL queries, so a row's 8 new frames are covered and 4 rows share a
 // wavefront; the key range is not split, so no partial results are merged.
@@ -568,10 +576,7 @@ constexpr int kDcQPL = 2;                        // queries per lane
 constexpr int kDcTW = 4;                         // temporal wavefronts per workgroup
 constexpr int kDcRows = 64 / (4 * kDcQH);        // rows per temporal wavefront
 constexpr int kDcBlockRows = kDcTW * kDcRows;    // rows per row block of a workgroup
-#ifndef CA2_DC_RING
-#define CA2_DC_RING 6
-#endif
-constexpr int kDcRing = CA2_DC_RING;             // keys in flight per temporal lane
+constexpr int kDcRing = 6;                       // keys in flight per temporal lane (register ring)
 
 // A wavefront-uniform barrier for wavefronts that share nothing through LDS
 // (they only keep count with the spatial wavefronts' barriers).
@@ -745,23 +750,6 @@ void denoise_call_kernel(SpatialArgs sa, TemporalArgs ta, int nblk) {
   }
 }
 
-// The same two halves in separate workgroups of one launch: blocks
-// [0, n_spatial) are spatial work items (4 computing wavefronts), blocks
-// [n_spatial, 2 n_spatial) temporal row blocks (kDcTW wavefronts, nblk row
-// blocks each). Both kinds fit on a CU together, and nothing couples their
-// progress.
-template <int D, int kStages, int kPF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void denoise_split_kernel(SpatialArgs sa, TemporalArgs ta, int n_spatial, int nblk) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * SCfg<D, 4>::STAGE];
-  if ((int)blockIdx.x < n_spatial) {
-    spatial_pipe<D, 1, 4, true, kStages, 1, false>(sa, xcd_work_index(blockIdx.x, n_spatial), threadIdx.x, smem);
-  } else {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    temporal_lockstep<D, kPF>(ta, wave, ((int)blockIdx.x - n_spatial) * nblk, nblk, 0);
-  }
-}
-
 // ----------------------------------------------------------------------------
 // fp32 kernel: one lane per query, K/V tiles of 32 keys in LDS
 // ----------------------------------------------------------------------------
@@ -928,15 +916,9 @@ hipError_t launch_denoise_call(int dtype, int d, const SpatialArgs& sa, const Te
   const int64_t nwg = (int64_t)((sa.tokens + 127) / 128) * sa.n * sa.heads * sa.batch;
   const int64_t blocks = ((int64_t)ta.rows_total + kDcBlockRows - 1) / kDcBlockRows;
   const int nblk = (int)((blocks + nwg - 1) / nwg);
-#ifdef CA2_DC_SPLIT
-  const dim3 grid((unsigned)(2 * nwg)), block(256);
-  if (d == 64) hipLaunchKernelGGL((denoise_split_kernel<64, 4, kDcRing>), grid, block, 0, s, sa, ta, (int)nwg, nblk);
-  else hipLaunchKernelGGL((denoise_split_kernel<72, 4, kDcRing>), grid, block, 0, s, sa, ta, (int)nwg, nblk);
-#else
   const dim3 grid((unsigned)nwg), block(64 * (4 + kDcTW));
   if (d == 64) hipLaunchKernelGGL((denoise_call_kernel<64, 4, kDcRing>), grid, block, 0, s, sa, ta, nblk);
   else hipLaunchKernelGGL((denoise_call_kernel<72, 4, kDcRing>), grid, block, 0, s, sa, ta, nblk);
-#endif
   return hipGetLastError();
 }
 
