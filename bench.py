@@ -300,12 +300,14 @@ SOURCES = {"spatial_prefix": "spatial_attn.hip", "spatial_self": "spatial_attn.h
 
 
 def source_hash(kernel):
-    """Hash of the kernel's source code with comments and whitespace removed
-    (a comment edit does not invalidate recorded counters)."""
+    """Hash of the kernel's source code and the device headers it includes,
+    with comments and whitespace removed (a comment edit does not invalidate
+    recorded counters)."""
     import re
-    p = os.path.join(ROOT, "causal_kv_cache_amd", "csrc", SOURCES[kernel])
-    with open(p) as f:
-        src = f.read()
+    src = ""
+    for name in (SOURCES[kernel], "device_common.hpp", "temporal_common.hpp"):
+        with open(os.path.join(ROOT, "causal_kv_cache_amd", "csrc", name)) as f:
+            src += f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
     src = re.sub(r"\s+", "", src)
@@ -508,6 +510,34 @@ def rollout_compare():
                                         "frac_mfma": round(fl_s / us_s / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)}}}
 
 
+def measured_ceilings():
+    """What the box sustains, beside the vendor figures: HBM from the
+    library's own cache-write copy kernel moving a 1.21 GB working set (well
+    past the 256 MB Infinity Cache: 64 batch entries x 8 frames of K and V,
+    read and written), and dense bf16 MFMA from the vendor GEMM (torch.matmul,
+    8192^3) -- the rate the matrix cores and the clock the part holds under
+    full MFMA load actually give."""
+    import torch
+    from causal_kv_cache_amd import ca2
+    B, H, d, S, l = 64, 16, 72, 256, 8
+    c = ca2.Cache(B, H, d, S, l, 8, 0, 16, "bf16")
+    kv = [torch.empty((B, l, S, H, d), dtype=torch.bfloat16, device="cuda").fill_(1.0) for _ in range(2)]
+    moved = 2 * 2 * B * l * S * H * d * 2          # K and V, read and written
+    us_copy = time_launches(lambda: c.ca2_cache_write(kv[0], kv[1], None, None), 10)
+    c.close()
+    del kv
+    n = 8192
+    a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    us_mm = time_launches(lambda: torch.matmul(a, b), 10)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbs": round(moved / us_copy / 1e3, 1), "hbm_copy_bytes": moved,
+            "mfma_bf16_gemm_tflops": round(2 * n ** 3 / us_mm / 1e6, 1),
+            "how": "HBM: ca2_cache_write copying 64 x 8 frames of K and V (read + write bytes / time); "
+                   "MFMA: torch.matmul bf16 8192^3 (vendor GEMM)"}
+
+
 def kernel_mode(kernel, workload, reps):
     """Launch one kernel of one workload `reps` times (for profilers)."""
     import torch
@@ -559,6 +589,45 @@ def cpu_baseline(budget_s: float):
             "seconds": el}
 
 
+def cpu_rollout():
+    """The oracle's 80-frame rollout (rollout_80f: B1, 256 tokens, 16 x 72,
+    chunk 8, P_max 41, P' 3; 1 conditioning frame + 10 AR steps, each 50
+    denoising calls and one cache-writing pass), float64 as it stands. A
+    whole rollout is 500 denoising calls (~3 min on 16 cores), so the sample
+    is one denoising call and one cache-writing pass at each distinct queue
+    length the rollout passes through (P_k = 1, 9, 17, 25, 33, 41), each
+    timed once in rollout order; the rollout time is their sum weighted by
+    the number of AR steps at that P_k. Returns seconds and the sample."""
+    import synth
+    from oracle import RolloutOracle
+    sh = dict(synth.WORKLOADS["rollout_80f"])
+    l = sh["l"]
+    o = RolloutOracle(sh, 2)
+    o.write(o.next_frames(1))
+    per_pk = {}
+    steps_at = {}
+    frames = 1
+    while frames < 81:
+        pk = o.queue.p_k
+        steps_at[pk] = steps_at.get(pk, 0) + 1
+        if pk not in per_pk:
+            t0 = time.perf_counter()
+            o.denoise_outputs(1 + frames // l, 0)
+            t1 = time.perf_counter()
+            o.write_pass_outputs(o.next_frames(l))
+            t2 = time.perf_counter()
+            per_pk[pk] = (t1 - t0, t2 - t1)
+        o.write(o.next_frames(l))
+        frames += l
+    total = sum(n * (50 * per_pk[pk][0] + per_pk[pk][1]) for pk, n in steps_at.items())
+    return {"seconds": round(total, 2),
+            "per_p_k_s": {str(pk): [round(a, 4), round(b, 4)] for pk, (a, b) in per_pk.items()},
+            "ar_steps_at_p_k": {str(k): v for k, v in steps_at.items()},
+            "sample": "one denoising call (temporal + prefix spatial attention) and one cache-writing pass "
+                      "(temporal + self spatial attention) per distinct P_k, float64; rollout = sum over AR "
+                      "steps of 50 calls + 1 pass at that step's P_k"}
+
+
 def cpu_per_kernel():
     """The oracle's temporal and prefix-spatial attention, as they stand
     (float64 numpy), timed per call on the host cores: whole calls at the
@@ -599,6 +668,91 @@ def cpu_per_kernel():
     return res
 
 
+TRAFFIC_KERNELS = {   # --kernel name -> (kernel-name substring, source file)
+    "cache_write": ("copy_frames_kernel", "cache_write.hip"),
+    "temporal": ("temporal_attn_ds_kernel", "temporal_attn.hip"),
+    "spatial_prefix": ("spatial_attn_pipe_kernel", "spatial_attn.hip"),
+    "spatial_self": ("spatial_attn_pipe_kernel", "spatial_attn.hip"),
+    "denoise_fused": ("denoise_call_kernel", "spatial_attn.hip"),
+    "qkv_proj": ("qkv_proj_kernel<false>", "qkv_proj.hip"),
+    "qkv_proj_stage": ("qkv_proj_kernel<true>", "qkv_proj.hip"),
+}
+
+
+def algorithmic_bytes(kernel, workload):
+    sh = WORKLOADS[workload]
+    n, pk, ps = sh["l"], sh["p_max"], sh["p_spatial"]
+    C = sh["H"] * sh["d"]
+    if kernel == "cache_write":
+        return write_bytes(sh, n)
+    if kernel == "temporal":
+        return temporal_bytes(sh, n, pk)
+    if kernel == "spatial_prefix":
+        return spatial_bytes(sh, n, ps)
+    if kernel == "spatial_self":
+        return spatial_bytes(sh, n, 0)
+    if kernel == "denoise_fused":
+        return spatial_bytes(sh, n, ps) + temporal_bytes(sh, n, pk)
+    m = sh["B"] * n * sh["S"]
+    x_w = 2 * (m * C + 3 * C * C)                      # X and W read once
+    if kernel == "qkv_proj":
+        return x_w + 2 * 3 * m * C                     # Q, K, V written
+    # fused stage: Q out, K/V into the ring, the last P' frames' K/V into the
+    # spatial buffer, the frames' TPE rows (fp32) read once
+    return x_w + 2 * 3 * m * C + 2 * 2 * sh["B"] * min(n, ps) * sh["S"] * C + 4 * n * 3 * C
+
+
+def traffic_summary(d, reps):
+    """profiles/traffic.json from rocprofv3 counter runs of `bench.py --kernel
+    K --workload W --reps R`: d/rd_K_W (TCC_EA0_RDREQ_sum, TCC_EA0_RDREQ_32B_sum,
+    TCC_EA0_RDREQ_64B_sum) and d/wr_K_W (WRITE_SIZE). Read bytes follow the
+    counters' definitions: RDREQ counts every L2-to-memory read request, of
+    32, 64 or 128 bytes, and the 32- and 64-byte ones are counted apart, so
+    bytes = 32 RDREQ_32B + 64 RDREQ_64B + 128 (RDREQ - RDREQ_32B - RDREQ_64B).
+    (The stock FETCH_SIZE expression prices every request that is neither
+    32-byte nor counted by TCC_BUBBLE at 64 bytes; on this part TCC_BUBBLE
+    reads 0 while the requests are 128-byte, so FETCH_SIZE is half the bytes
+    read -- the copy kernel's known 51,904,512 bytes confirm 128 per request.)
+    Write bytes are WRITE_SIZE (64- and 32-byte write requests, priced as
+    such). Means over the last `reps` dispatches of the kernel (the timed
+    launches)."""
+    import csv
+    import collections
+
+    def means(path, name):
+        rows = list(csv.DictReader(open(os.path.join(path, "run_counter_collection.csv"))))
+        by = collections.defaultdict(list)
+        for r in rows:
+            if name in r["Kernel_Name"]:
+                by[r["Counter_Name"]].append(float(r["Counter_Value"]))
+        return {k: sum(v[-reps:]) / len(v[-reps:]) for k, v in by.items()}, \
+            next((r["Kernel_Name"] for r in rows if name in r["Kernel_Name"]), "")
+
+    out = {"method": traffic_summary.__doc__.split("\n\n")[0].replace("\n", " "), "kernels": {}}
+    for entry in sorted(os.listdir(d)):
+        if not entry.startswith("rd_") or entry.endswith(".log"):
+            continue
+        tag = entry[3:]
+        kernel = next(k for k in sorted(TRAFFIC_KERNELS, key=len, reverse=True) if tag.startswith(k + "_"))
+        workload = tag[len(kernel) + 1:]
+        name, src = TRAFFIC_KERNELS[kernel]
+        rd, kname = means(os.path.join(d, entry), name)
+        wr, _ = means(os.path.join(d, "wr_" + tag), name)
+        r, r32, r64 = rd["TCC_EA0_RDREQ_sum"], rd["TCC_EA0_RDREQ_32B_sum"], rd["TCC_EA0_RDREQ_64B_sum"]
+        read = 32 * r32 + 64 * r64 + 128 * (r - r32 - r64)
+        write = wr["WRITE_SIZE"] * 1024
+        alg = algorithmic_bytes(kernel, workload)
+        out["kernels"][f"{kernel}@{workload}"] = {
+            "kernel_name": kname, "rdreq": round(r), "rdreq_32b": round(r32), "rdreq_64b": round(r64),
+            "read_bytes": round(read), "write_size_kib": round(wr["WRITE_SIZE"], 1),
+            "hbm_bytes_per_launch": round(read + write), "algorithmic_bytes": alg,
+            "ratio_to_algorithmic": round((read + write) / alg, 3),
+            "source": src, "source_sha256_16": source_hash(kernel)}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -612,9 +766,14 @@ def main():
     ap.add_argument("--kernel", choices=KERNELS, help="only launch this kernel (profiling mode)")
     ap.add_argument("--workload", choices=tuple(WORKLOADS), default=AR_STEP["name"])
     ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--traffic-summary", metavar="DIR",
+                    help="write profiles/traffic.json from rocprofv3 counter runs in DIR (no GPU needed)")
     ap.add_argument("--spatial-variant", type=int, default=0,
                     help="profiling mode: force the bf16 spatial launch variant (0 = by size)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        print(json.dumps(traffic_summary(args.traffic_summary, args.reps), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -679,6 +838,14 @@ def main():
     }
     del w
     torch.cuda.empty_cache()
+    ceil = measured_ceilings()
+    for r in result["kernels"].values():
+        meas = ceil["hbm_copy_gbs"] if r["bound"] == "hbm" else ceil["mfma_bf16_gemm_tflops"]
+        r["frac_of_measured"] = round(r["achieved"] / meas, 4)
+    result["measured_ceilings"] = ceil
+    result["roofline"]["measured_peak"] = (ceil["hbm_copy_gbs"] if roofline["bound"] == "hbm"
+                                           else ceil["mfma_bf16_gemm_tflops"])
+    result["roofline"]["frac_of_measured"] = round(roofline["achieved"] / result["roofline"]["measured_peak"], 4)
 
     if not args.no_large:
         wl = Workload(LARGE, 2, seed=99)
@@ -707,6 +874,13 @@ def main():
                 if name in gpu.get(wl, {}):
                     r[key] = round(gpu[wl][name]["us"], 3)
         cb["per_kernel"] = per
+        ro = cpu_rollout()
+        gpu_ro = result.get("rollout_cached_vs_recompute")
+        if gpu_ro:
+            # the GPU figure for the same rollout: one attention layer's share of the timed 8-layer rollout
+            ro["gpu_seconds_one_layer"] = round(gpu_ro["steps"][-1]["cumulative_cached_ms"] / 1e3 /
+                                                gpu_ro["layers"], 4)
+        cb["rollout_80f"] = ro
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
