@@ -127,19 +127,26 @@ class Workload:
         self.passes = 0
         torch.cuda.synchronize()
 
+    def temporal_set(self, i):
+        """The temporal layer's Q/K/V of call i: another set than the spatial
+        layer's, so the two halves of a call read independent tensors."""
+        return self.sets[(i + len(self.sets) // 2) % len(self.sets)]
+
     def denoise(self, i):
         """One denoising call: prefix spatial + causal temporal attention over
         one cache, fused into one launch where the shapes allow it."""
         q, k, v = self.sets[i % len(self.sets)]
+        qt, kt, vt = self.temporal_set(i)
         c = self.caches[i % len(self.caches)]
-        c.ca2_denoise_attn(q, k, v, self.out_s, q, k, v, self.out_t)
+        c.ca2_denoise_attn(q, k, v, self.out_s, qt, kt, vt, self.out_t)
 
     def denoise_two_launches(self, i):
         """The same call as two launches (stand-alone spatial, then temporal)."""
         q, k, v = self.sets[i % len(self.sets)]
+        qt, kt, vt = self.temporal_set(i)
         c = self.caches[i % len(self.caches)]
         c.ca2_spatial_attn(q, k, v, self.out_s)
-        c.ca2_temporal_attn(q, k, v, self.out_t)
+        c.ca2_temporal_attn(qt, kt, vt, self.out_t)
 
     def write_pass(self):
         from causal_kv_cache_amd import ca2
@@ -237,7 +244,8 @@ def launchers(w: Workload):
 
     def k_denoise_fused():
         c, (q, k, v) = nxt()
-        c.ca2_denoise_attn(q, k, v, w.out_s, q, k, v, w.out_t)
+        qt, kt, vt = w.temporal_set(idx[0])
+        c.ca2_denoise_attn(q, k, v, w.out_s, qt, kt, vt, w.out_t)
 
     return {"spatial_prefix": k_spatial, "temporal": k_temporal, "spatial_self": k_spatial_self,
             "denoise_fused": k_denoise_fused}
