@@ -44,6 +44,7 @@ constexpr int OPB = TN * ROWB;          // one operand tile
 constexpr int STAGE = 2 * OPB;          // W tile, then X tile
 constexpr int kStages = 2;
 constexpr int kThreads = 512;
+constexpr int kGroupM = 8;              // token panels per tile group (see the work order below)
 constexpr int kWaves = kThreads / 64;
 constexpr int NI = TN * kSlots / 64;    // copy instructions per operand per k-tile (36)
 constexpr int kPer = 2 * NI / kWaves;   // per wavefront per k-tile (9)
@@ -59,9 +60,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int wn = wave & 1, wm = wave >> 1;       // 128 channels x 64 tokens per wavefront
   const int N = 3 * a.c_out;
   const int tiles_n = (N + TN - 1) / TN;
+  // Tiles in groups of kGroupM token panels: within a group the token panel
+  // runs fastest, so a run of consecutive work items (what one XCD holds at
+  // once, dealt by xcd_work_index) covers kGroupM token panels x a few
+  // channel panels and each panel's k-slab is read once into that XCD's L2.
   const int w = xcd_work_index(blockIdx.x, gridDim.x);
-  const int n0 = (w % tiles_n) * TN;
-  const int m0 = (w / tiles_n) * TM;
+  const int tiles_m = (a.m + TM - 1) / TM;
+  const int grp = w / (kGroupM * tiles_n);
+  const int gm = min(kGroupM, tiles_m - grp * kGroupM);   // token panels in this group
+  const int wi = w - grp * kGroupM * tiles_n;
+  const int n0 = (wi / gm) * TN;
+  const int m0 = (grp * kGroupM + wi % gm) * TM;
   const int KT = a.c_in / TK;
 
   // per-lane copy offsets (bytes from the k-tile base) for this wavefront's
