@@ -14,8 +14,14 @@
 //     shared with the partner lane (lane ^ 32) by one exchange, and the
 //     exponentiated scores are already laid out as the B operand of
 //     O^T = V^T P^T -- they never leave registers;
-//   * online softmax in base 2 (scale * log2 e folded into one FMA), fp32
-//     statistics, P rounded to bf16 for the PV product, fp32 accumulators;
+//   * online softmax in base 2, fp32 statistics, P rounded to bf16 for the
+//     PV product, fp32 accumulators. Where d % 16 == 8 (d = 72) the last
+//     16-dim QK step is half padding; there Q is multiplied by
+//     scale * log2 e once (rounded to bf16) and the padding carries the
+//     running maximum as one more product term (-m times a key entry of 1),
+//     so the product yields the shifted base-2 scores and P is exp2 of the
+//     MFMA output with no other per-score arithmetic. Elsewhere the scale
+//     and the maximum enter through one FMA per score;
 //     the V row padding holds 1.0 at dim d, so row d of O^T is the softmax
 //     normaliser, computed by the MFMA from the same bf16 P as the numerator.
 // The fp32 path (for fp32 caches) is a plain LDS-tiled VALU kernel.
@@ -106,6 +112,39 @@ __device__ __forceinline__ void lazy_rescale(float mx_raw, float c, float& m_run
     for (int r = 0; r < 16; ++r) acc[i][r] *= corr;
 }
 
+// The same for scores that the product already shifts (d % 16 == 8): the
+// product yields y = c s - m_run (the running maximum enters it as a sum of
+// three bf16 terms, which hold a float32 value exactly), so P = exp2(y) and
+// the threshold is kLazy itself (-inf: no score seen yet; m_run is then 0).
+// The caller puts the new maximum's three bf16 terms into its Q operand and
+// scores the chunk again.
+template <int DBLK>
+__device__ __forceinline__ void lazy_rescale_shifted(float mx, float& m_run, float& thr, float& l_run,
+                                                     f32x16 (&acc)[DBLK]) {
+  const bool need = mx > thr;          // the caller has seen some lane need it
+  const bool have = thr != -INFINITY;
+  const float m_new = need ? m_run + mx : m_run;
+  const float corr = !need ? 1.f : have ? fast_exp2(m_run - m_new) : 0.f;   // 0: acc, l_run still 0
+  thr = need ? kLazy : thr;
+  m_run = m_new;
+  l_run *= corr;
+#pragma unroll
+  for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] *= corr;
+}
+
+// -m as three bf16 terms whose sum is -m (a float32 has 24 significant bits,
+// a bf16 8), packed as the first three entries of a bf16x8 Q operand slice.
+__device__ __forceinline__ uint2 neg_bf16x3(float m) {
+  const float x = -m;
+  const float h = __builtin_bit_cast(float, pack_bf16x2(x, 0.f) << 16);
+  const float r1 = x - h;
+  const float md = __builtin_bit_cast(float, pack_bf16x2(r1, 0.f) << 16);
+  const float r2 = r1 - md;
+  return make_uint2(pack_bf16x2(h, md), pack_bf16x2(r2, 0.f));
+}
+
 // ----------------------------------------------------------------------------
 // bf16 MFMA kernel, software-pipelined
 // ----------------------------------------------------------------------------
@@ -169,6 +208,11 @@ __device__ __forceinline__ void spatial_pipe(const SpatialArgs& a, int w, int ti
   const int kh = wave / G;                         // with KS == 2: key half of every tile
   const int q_base = qblk * (32 * QB * G) + grp * (32 * QB);
 
+  // kShifted (d % 16 == 8): the upper half of the last QK step is padding;
+  // there the Q operand holds -m_run as three bf16 terms (lanes of the upper
+  // half, first three entries) against key entries of 1.0, and the rest of
+  // Q holds c q
+  constexpr bool kShifted = D % 16 == 8;
   bf16x8v qop[QB][KSTEPS];
   bool q_ok[QB];
 #pragma unroll
@@ -179,8 +223,15 @@ __device__ __forceinline__ void spatial_pipe(const SpatialArgs& a, int w, int ti
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       const int d0 = 16 * s + 8 * half;
-      uint4 u = make_uint4(0, 0, 0, 0);
+      uint4 u = make_uint4(0, 0, 0, 0);   // the upper half's shift terms start at m_run = 0
       if (!producer && q_ok[qb] && d0 < D) u = *reinterpret_cast<const uint4*>(qp + d0);
+      if constexpr (kShifted) {           // c q, rounded once to bf16
+        float qf[8];
+        Elem<bf16_t>::unpack(u, qf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[e] *= a.scale_log2e;
+        u = Elem<bf16_t>::pack(qf);
+      }
       qop[qb][s] = __builtin_bit_cast(bf16x8v, u);
     }
   }
@@ -307,20 +358,42 @@ __device__ __forceinline__ void spatial_pipe(const SpatialArgs& a, int w, int ti
       for (int r = 0; r < 16; ++r) acc[qb][i][r] = 0.f;
   float m_run[QB], l_run[QB], thr[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = kNoMax; l_run[qb] = 0.f; thr[qb] = (kNoMax + kLazy) / a.scale_log2e; }
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = kShifted ? 0.f : kNoMax;
+    l_run[qb] = 0.f;
+    thr[qb] = kShifted ? -INFINITY : (kNoMax + kLazy) / a.scale_log2e;
+  }
 
   const f32x16 zero16 = {};
-  // S^T = K Q^T for keys kb*32 .. +31 of a tile: sc[qb] register r holds key
-  // kb*32 + 8(r/4) + 4*half + r%4 of query 32*qb + col
+  // S^T = K Q^T for keys kb*32 .. +31 of a tile (kShifted: c K Q^T - m_run):
+  // sc[qb] register r holds key kb*32 + 8(r/4) + 4*half + r%4 of query 32*qb + col
   auto qk = [&](const unsigned char* ks, int kb, f32x16 (&sc)[QB]) {
     const unsigned char* krow = ks + (kb * 32 + col) * C::KROW;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      const bf16x8v kop = *reinterpret_cast<const bf16x8v*>(krow + (16 * s + 8 * half) * 2);
+      bf16x8v kop = *reinterpret_cast<const bf16x8v*>(krow + (16 * s + 8 * half) * 2);
+      if (kShifted && s == KSTEPS - 1)      // the padding half: key entries 1.0 against -m_run
+        kop = half ? __builtin_bit_cast(bf16x8v, make_uint4(0x3F803F80u, 0x3F80u, 0, 0)) : kop;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[qb][s], s == 0 ? zero16 : sc[qb], 0, 0, 0);
     }
+  };
+  // the same for one query block (re-scoring after a raise)
+  auto qk1 = [&](const unsigned char* ks, int kb, int qb, f32x16& sc) {
+    const unsigned char* krow = ks + (kb * 32 + col) * C::KROW;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      bf16x8v kop = *reinterpret_cast<const bf16x8v*>(krow + (16 * s + 8 * half) * 2);
+      if (kShifted && s == KSTEPS - 1)
+        kop = half ? __builtin_bit_cast(bf16x8v, make_uint4(0x3F803F80u, 0x3F80u, 0, 0)) : kop;
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[qb][s], s == 0 ? zero16 : sc, 0, 0, 0);
+    }
+  };
+  auto mask1 = [&](f32x16& sc, int kb, int nk) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= nk) sc[r] = -INFINITY;
   };
   auto mask_tail = [&](f32x16 (&sc)[QB], int kb, int nk) {
 #pragma unroll
@@ -329,17 +402,36 @@ __device__ __forceinline__ void spatial_pipe(const SpatialArgs& a, int w, int ti
       for (int r = 0; r < 16; ++r)
         if (kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= nk) sc[qb][r] = -INFINITY;
   };
-  // chunk max (scaled, base 2) and lazy rescale of the running state
-  auto max_rescale = [&](const f32x16 (&sc)[QB]) {
+  // chunk max (base 2; kShifted: of the shifted scores) and lazy rescale of
+  // the running state. kShifted: a raise re-scores the chunk (keys kb*32 ..
+  // +31 of the tile at ks, nk keys valid) with the new maximum in the
+  // product, so that every chunk's scores come out of the same arithmetic --
+  // scores of equal keys stay bitwise equal whatever their magnitude.
+  auto max_rescale = [&](f32x16 (&sc)[QB], const unsigned char* ks, int kb, int nk) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = __builtin_fmaxf(sc[qb][0], sc[qb][1]);
 #pragma unroll
       for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[qb][r]), sc[qb][r + 1]);
-      lazy_rescale(max_halves(mx), a.scale_log2e, m_run[qb], thr[qb], l_run[qb], acc[qb]);
+      mx = max_halves(mx);
+      if constexpr (kShifted) {
+        if (__builtin_amdgcn_ballot_w64(mx > thr[qb]) != 0) {
+          lazy_rescale_shifted(mx, m_run[qb], thr[qb], l_run[qb], acc[qb]);
+          uint4 u = __builtin_bit_cast(uint4, qop[qb][KSTEPS - 1]);
+          const uint2 t = neg_bf16x3(m_run[qb]);
+          u.x = half ? t.x : u.x;
+          u.y = half ? t.y : u.y;
+          qop[qb][KSTEPS - 1] = __builtin_bit_cast(bf16x8v, u);
+          qk1(ks, kb, qb, sc[qb]);
+          if (!FULL) mask1(sc[qb], kb, nk);
+        }
+      } else {
+        lazy_rescale(mx, a.scale_log2e, m_run[qb], thr[qb], l_run[qb], acc[qb]);
+      }
     }
   };
-  // P of one chunk as the B operands of two 16-key k-steps
+  // P of one chunk as the B operands of two 16-key k-steps (kShifted: exp2 of
+  // the scores as they stand)
   auto expc = [&](const f32x16 (&sc)[QB], bf16x8v (&pf)[QB][2]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -349,8 +441,13 @@ __device__ __forceinline__ void spatial_pipe(const SpatialArgs& a, int w, int ti
         uint32_t wv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(fmaf(sc[qb][8 * h2 + 2 * e], a.scale_log2e, mneg));
-          const float p1 = fast_exp2(fmaf(sc[qb][8 * h2 + 2 * e + 1], a.scale_log2e, mneg));
+          float x0 = sc[qb][8 * h2 + 2 * e], x1 = sc[qb][8 * h2 + 2 * e + 1];
+          if constexpr (!kShifted) {
+            x0 = fmaf(x0, a.scale_log2e, mneg);
+            x1 = fmaf(x1, a.scale_log2e, mneg);
+          }
+          const float p0 = fast_exp2(x0);
+          const float p1 = fast_exp2(x1);
           if constexpr (!C::ONES) l_run[qb] += p0 + p1;
           wv[e] = pack_bf16x2(p0, p1);
         }
@@ -408,7 +505,7 @@ __device__ __forceinline__ void spatial_pipe(const SpatialArgs& a, int w, int ti
   int nk_t = min(kBN, S);             // keys in tile t
   qk(smem, KS == 2 ? kh : 0, s0);
   if (!FULL && nk_t < (KS == 2 ? kBN : 32)) mask_tail(s0, KS == 2 ? kh : 0, nk_t);
-  max_rescale(s0);
+  max_rescale(s0, smem, KS == 2 ? kh : 0, nk_t);
 
   int st_r = 0;                       // stage of tile t
   int t0_n = kBN >= S ? 0 : kBN;      // first key of tile t+1 within its frame
@@ -421,7 +518,7 @@ __device__ __forceinline__ void spatial_pipe(const SpatialArgs& a, int w, int ti
       expc(s0, pf);
       pv(vs, 0, pf);
       if (!FULL && nk_t < kBN) mask_tail(s1, 1, nk_t);
-      max_rescale(s1);
+      max_rescale(s1, ks, 1, nk_t);
       st_r = st_r == kStages - 1 ? 0 : st_r + 1;
       if constexpr (!PROD) wait_tiles(min(kStages - 3, n_tiles - t - 2));   // tile t+1; younger tiles stay in flight
       lds_barrier();                                    // every wavefront is done with tile t-1
@@ -433,7 +530,7 @@ __device__ __forceinline__ void spatial_pipe(const SpatialArgs& a, int w, int ti
       pv(vs, 1, pf);
       nk_t = min(kBN, S - t0_n);
       if (!FULL && nk_t < 32) mask_tail(s0, 0, nk_t);
-      max_rescale(s0);
+      max_rescale(s0, smem + st_r * C::STAGE, 0, nk_t);
       t0_n = t0_n + kBN >= S ? 0 : t0_n + kBN;
     }
     {  // last tile
@@ -443,7 +540,7 @@ __device__ __forceinline__ void spatial_pipe(const SpatialArgs& a, int w, int ti
       expc(s0, pf);
       pv(vs, 0, pf);
       if (!FULL && nk_t < kBN) mask_tail(s1, 1, nk_t);
-      max_rescale(s1);
+      max_rescale(s1, ks, 1, nk_t);
       expc(s1, pf);
       pv(vs, 1, pf);
     }
@@ -461,7 +558,7 @@ __device__ __forceinline__ void spatial_pipe(const SpatialArgs& a, int w, int ti
       pv(vs, kh, pf);
       nk_t = min(kBN, S - t0_n);
       if (!FULL && nk_t < kBN) mask_tail(sb, kh, nk_t);
-      max_rescale(sb);
+      max_rescale(sb, smem + st_r * C::STAGE, kh, nk_t);
       t0_n = t0_n + kBN >= S ? 0 : t0_n + kBN;
     };
     auto last = [&](const f32x16 (&sa)[QB]) {
@@ -488,7 +585,7 @@ __device__ __forceinline__ void spatial_pipe(const SpatialArgs& a, int w, int ti
         for (int i = 0; i < DBLK; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) d[(i * 16 + r) * 64] = acc[qb][i][r];
-        d[(DBLK * 16) * 64] = m_run[qb];
+        d[(DBLK * 16) * 64] = kShifted && thr[qb] == -INFINITY ? kNoMax : m_run[qb];
         d[(DBLK * 16 + 1) * 64] = l_run[qb];
       }
     }
@@ -498,8 +595,9 @@ __device__ __forceinline__ void spatial_pipe(const SpatialArgs& a, int w, int ti
     for (int qb = 0; qb < QB; ++qb) {
       const float* d = mg + qb * (DBLK * 16 + 2) * 64 + lane;
       const float m_o = d[(DBLK * 16) * 64];
-      const float m_new = __builtin_fmaxf(m_run[qb], m_o);
-      const float c_me = fast_exp2(m_run[qb] - m_new), c_o = fast_exp2(m_o - m_new);
+      const float m_me = kShifted && thr[qb] == -INFINITY ? kNoMax : m_run[qb];
+      const float m_new = __builtin_fmaxf(m_me, m_o);
+      const float c_me = fast_exp2(m_me - m_new), c_o = fast_exp2(m_o - m_new);
 #pragma unroll
       for (int i = 0; i < DBLK; ++i)
 #pragma unroll
@@ -871,7 +969,9 @@ hipError_t launch_mfma(const SpatialArgs& a, hipStream_t s) {
   const int64_t frames = (int64_t)a.n * a.heads * a.batch;
   const int64_t wg_big = (int64_t)((a.tokens + 255) / 256) * frames;
   const int64_t wg_small = (int64_t)((a.tokens + 127) / 128) * frames;
-  int cfg = wg_big >= 1024 ? 2 : D == 72 && wg_small <= device_cus() ? 4 : 1;
+  // (the 64-query form only over whole 64-key tiles: with partial tiles its
+  // register budget is exceeded)
+  int cfg = wg_big >= 1024 && a.tokens % kBN == 0 ? 2 : D == 72 && wg_small <= device_cus() ? 4 : 1;
   if (const int force = g_forced_variant.load(std::memory_order_relaxed)) cfg = force;
   if constexpr (D <= 72) {
     if (cfg == 2) return launch_pipe_cfg<D, 2, 4, 4, 1>(a, s);

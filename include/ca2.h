@@ -184,10 +184,11 @@ ca2_status ca2_temporal_attn(const ca2_cache* cache, const void* q, const void* 
  * CA2_SPATIAL_SELF: keys/values are the frame's own S tokens (the clean-frame
  *   self-repeat case, whose value equals plain self-attention).
  * q, k, v, out: [B][n][S][H][d]. 1 <= n_frames <= chunk; scale > 0 and
- * finite. bf16: the scores must satisfy |scale * q . k| < 1e9 (the kernel
- * evaluates exp2(s c - m) with one fused multiply-add, whose rounding
- * residue -- a factor common to every P of a row, so it cancels -- stays far
- * from overflow below that).
+ * finite. bf16: the scores must satisfy |scale * q . k| < 1e9 (they are
+ * formed in float32 with the running maximum subtracted -- by one fused
+ * multiply-add per score, or at head_dim 72 inside the matrix product, whose
+ * Q operand is then q * scale * log2(e) rounded once to bf16 -- and equal
+ * keys keep bitwise equal scores at any magnitude below that).
  */
 ca2_status ca2_spatial_attn(const ca2_cache* cache, const void* q, const void* k,
                             const void* v, void* out, int32_t n_frames, int32_t mode,
