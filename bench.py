@@ -275,6 +275,15 @@ def kernel_table(w: Workload, reps: int, fused: bool = False):
     by = temporal_bytes(sh, n, pk)
     rows["temporal_attn"] = dict(us=us, us_min=lo, us_max=hi, flops=temporal_flops(sh, n, pk), bytes=by,
                                  bound="hbm", achieved=by / us / 1e3, peak=HBM_PEAK_GBS, unit="GB/s")
+    # the other bf16 temporal kernel (whole rows on the matrix cores), for comparison
+    from causal_kv_cache_amd import ca2
+    ca2.ca2_set_temporal_variant(2)
+    try:
+        us, lo, hi = time_launches_stats(k_temporal, reps)
+    finally:
+        ca2.ca2_set_temporal_variant(0)
+    rows["temporal_attn_mfma_rows"] = dict(us=us, us_min=lo, us_max=hi, flops=temporal_flops(sh, n, pk), bytes=by,
+                                           bound="hbm", achieved=by / us / 1e3, peak=HBM_PEAK_GBS, unit="GB/s")
     us, lo, hi = time_launches_stats(k_spatial_self, max(4, reps // 4))
     fl = spatial_flops(sh, n, 0)
     rows["spatial_attn_self"] = dict(us=us, us_min=lo, us_max=hi, flops=fl, bytes=spatial_bytes(sh, n, 0),
@@ -780,6 +789,9 @@ def main():
                     help="write profiles/traffic.json from rocprofv3 counter runs in DIR (no GPU needed)")
     ap.add_argument("--spatial-variant", type=int, default=0,
                     help="profiling mode: force the bf16 spatial launch variant (0 = by size)")
+    ap.add_argument("--temporal-variant", type=int, default=0,
+                    help="profiling mode: force the bf16 temporal kernel (0 = default dimension-split, "
+                         "2 = matrix-core rows)")
     args = ap.parse_args()
     if args.traffic_summary:
         print(json.dumps(traffic_summary(args.traffic_summary, args.reps), indent=1))
@@ -795,6 +807,7 @@ def main():
     torch.cuda.set_device(0)
     if args.kernel:
         ca2.ca2_set_spatial_variant(args.spatial_variant)
+        ca2.ca2_set_temporal_variant(args.temporal_variant)
         print(json.dumps(kernel_mode(args.kernel, args.workload, args.reps)), flush=True)
         return
 

@@ -26,7 +26,7 @@ CA2_SPATIAL_PREFIX = 0
 CA2_SPATIAL_SELF = 1
 CA2_STAGE_RING = 1
 CA2_STAGE_SPATIAL = 2
-ABI_VERSION = 3      # include/ca2.h CA2_ABI_VERSION this binding is written for
+ABI_VERSION = 4      # include/ca2.h CA2_ABI_VERSION this binding is written for
 
 _DTYPES = {"f32": CA2_F32, "bf16": CA2_BF16}
 
@@ -79,6 +79,7 @@ _SIGS = {
     "ca2_toy_ln_mod": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P]),
     "ca2_toy_linear": (_I32, [_P, _I32, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _P]),
     "ca2_set_spatial_variant": (_I32, [_I32]),
+    "ca2_set_temporal_variant": (_I32, [_I32]),
     "ca2_abi_version": (_I32, []),
     "ca2_status_string": (ctypes.c_char_p, [_I32]),
     "ca2_last_error": (ctypes.c_char_p, []),
@@ -155,6 +156,11 @@ def make_config(B, H, d, S, l, p_max, p_spatial, tpe_len, dtype) -> Ca2Config:
 def ca2_set_spatial_variant(variant: int):
     """Force the bf16 spatial kernel's launch variant (0 = by grid size)."""
     _check(load().ca2_set_spatial_variant(int(variant)), "ca2_set_spatial_variant")
+
+
+def ca2_set_temporal_variant(variant: int):
+    """Force the bf16 temporal kernel (0, 1 = dimension-split, the default; 2 = matrix-core rows)."""
+    _check(load().ca2_set_temporal_variant(int(variant)), "ca2_set_temporal_variant")
 
 
 def ca2_tpe_index_raw(first_frame: int, n: int, tpe_len: int):

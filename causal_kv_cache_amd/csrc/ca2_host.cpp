@@ -454,6 +454,12 @@ ca2_status ca2_set_spatial_variant(int32_t variant) {
   return ok();
 }
 
+ca2_status ca2_set_temporal_variant(int32_t variant) {
+  if (variant < 0 || variant > 2) return fail(CA2_ERR_INVALID_ARG, "variant %d not in [0, 2]", variant);
+  ca2::set_temporal_variant(variant);
+  return ok();
+}
+
 ca2_status ca2_tpe_index_raw(int64_t first, int32_t n, int32_t L, int32_t* out) {
   if (first < 0 || n < 0 || L < 1) return fail(CA2_ERR_INVALID_ARG, "first >= 0, n >= 0, tpe_len >= 1");
   if (n > 0 && !out) return fail(CA2_ERR_INVALID_ARG, "host_out is NULL");

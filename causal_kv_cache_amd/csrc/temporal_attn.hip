@@ -27,11 +27,27 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "temporal_common.hpp"
+#include "temporal_mfma.hpp"
+
+#include <atomic>
 
 namespace ca2 {
 namespace {
 
 constexpr int kWaves = 4;              // wavefronts per workgroup
+
+// Compute units of the current device (queried once per device).
+int device_cus_t() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 constexpr int kStageBudget = 20480;    // LDS bytes per wavefront for K+V staging
 
 template <typename T, int D, int QL>
@@ -498,6 +514,44 @@ hipError_t launch_ds(const TemporalArgs& a, hipStream_t s) {
   return launch_ds_q<D, 4>(a, s);
 }
 
+// ----------------------------------------------------------------------------
+// bf16 kernel on the matrix cores: whole rows per wavefront (selectable)
+// ----------------------------------------------------------------------------
+// Each wavefront computes `rpw` consecutive rows with temporal_mfma_rows
+// (scores, the transposition of V and O = P V on v_mfma_f32_16x16x32_bf16,
+// 32 keys per step, one step's loads in flight while the previous step is
+// computed). Up to 16 query frames per row. Rows per wavefront are chosen so
+// that the launch is about one round of two wavefronts per SIMD (the register
+// budget), which keeps eight steps' K/V in flight per compute unit. It cuts
+// the VALU work per row about fourfold but is slower than the dimension-split
+// kernel: a wavefront reads one row's keys at a time (16 scattered 64-byte
+// pieces per load instead of whole runs of adjacent rows) and each 32-key
+// step is a dependent chain of MFMAs, two cross-lane exchanges and the
+// exponentials, so it is only run when forced (ca2_set_temporal_variant(2)).
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void temporal_mfma_kernel(TemporalArgs a, int rpw) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int first = (blockIdx.x * 4 + wave) * rpw;
+  const int rows = max(0, min(rpw, a.rows_total - first));
+  temporal_mfma_rows<D>(a, [&](int i) { return first + i; }, rows, 0);
+}
+
+template <int D>
+hipError_t launch_tm(const TemporalArgs& a, hipStream_t s) {
+  const int waves_target = 8 * device_cus_t();
+  int rpw = (a.rows_total + waves_target - 1) / waves_target;
+  rpw = rpw < 1 ? 1 : rpw;
+  const int64_t waves = ((int64_t)a.rows_total + rpw - 1) / rpw;
+  const int64_t wgs = (waves + 3) / 4;
+  if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((temporal_mfma_kernel<D>), dim3((unsigned)wgs), dim3(256), 0, s, a, rpw);
+  return hipGetLastError();
+}
+
+// Launch variant forced by ca2_set_temporal_variant (0 = chosen by shape).
+std::atomic<int> g_forced_temporal{0};
+
 template <typename T, int D>
 hipError_t launch_td(const TemporalArgs& a, hipStream_t s) {
   const int ql = a.n <= 4 ? 4 : a.n <= 8 ? 8 : 16;
@@ -535,13 +589,19 @@ hipError_t launch_temporal(int dtype, int d, const TemporalArgs& a, hipStream_t 
       case 128: return launch_td<float, 128>(a, s);
     }
   } else if (dtype == 1) {
+    // the dimension-split kernel; the matrix-core rows only when forced
+    // (they measured slower at every shape: the 256-token call 16.7 vs
+    // 14.7 us, the 32x32-latent batch 435 vs 318 us)
+    const bool mfma = g_forced_temporal.load(std::memory_order_relaxed) == 2;
     switch (d) {
-      case 64: return launch_ds<64>(a, s);
-      case 72: return launch_ds<72>(a, s);
+      case 64: return mfma && a.n <= kTmMaxQ ? launch_tm<64>(a, s) : launch_ds<64>(a, s);
+      case 72: return mfma && a.n <= kTmMaxQ ? launch_tm<72>(a, s) : launch_ds<72>(a, s);
       case 128: return launch_ds<128>(a, s);
     }
   }
   return hipErrorInvalidValue;
 }
+
+void set_temporal_variant(int v) { g_forced_temporal.store(v, std::memory_order_relaxed); }
 
 }  // namespace ca2

@@ -388,10 +388,22 @@ ca2_status ca2_toy_linear(const float* x, int32_t ldx, const float* w, int32_t l
  */
 ca2_status ca2_set_spatial_variant(int32_t variant);
 
+/*
+ * Test and measurement switch: force the kernel of bf16 temporal attention
+ * (ca2_temporal_attn, ca2_temporal_attn_frames, and the temporal half of
+ * ca2_denoise_attn when it runs as two launches) for every later call in the
+ * process: 0 = the default (the dimension-split kernel: VALU dot products),
+ * 1 = the same, 2 = matrix-core rows wherever they apply (n <= 16, head_dim
+ * 64 or 72; slower, kept for comparison). Every choice computes the same
+ * attention. INVALID_ARG outside [0, 2]. Not synchronised with calls in
+ * flight on other host threads.
+ */
+ca2_status ca2_set_temporal_variant(int32_t variant);
+
 /* Version of this ABI (entry points, argument lists, struct layouts):
  * CA2_ABI_VERSION. A binding compares it with the value it was written for
  * and refuses a library built from other sources. */
-#define CA2_ABI_VERSION 3
+#define CA2_ABI_VERSION 4
 int32_t ca2_abi_version(void);
 
 /* Static description of a status code; any other integer gives

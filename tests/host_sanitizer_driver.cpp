@@ -80,6 +80,9 @@ int main() {
   CHECK(ca2_set_spatial_variant(-1) == CA2_ERR_INVALID_ARG);
   CHECK(ca2_set_spatial_variant(5) == CA2_ERR_INVALID_ARG);
   for (int32_t v = 4; v >= 0; --v) CHECK(ca2_set_spatial_variant(v) == CA2_OK);
+  CHECK(ca2_set_temporal_variant(-1) == CA2_ERR_INVALID_ARG);
+  CHECK(ca2_set_temporal_variant(3) == CA2_ERR_INVALID_ARG);
+  for (int32_t v = 2; v >= 0; --v) CHECK(ca2_set_temporal_variant(v) == CA2_OK);
 
   // status strings
   for (int32_t s = 0; s <= 5; ++s) CHECK(std::strlen(ca2_status_string(s)) > 0);

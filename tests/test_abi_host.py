@@ -197,6 +197,14 @@ def test_abi_version_matches_header(lib):
     assert lib.load().ca2_abi_version() == declared == lib.ABI_VERSION
 
 
+def test_temporal_variant_switch_range(lib):
+    raw = lib.load()
+    assert raw.ca2_set_temporal_variant(-1) == lib.CA2_ERR_INVALID_ARG
+    assert raw.ca2_set_temporal_variant(3) == lib.CA2_ERR_INVALID_ARG
+    for v in (2, 1, 0):
+        assert raw.ca2_set_temporal_variant(v) == lib.CA2_OK
+
+
 def test_spatial_variant_switch_range(lib):
     raw = lib.load()
     assert raw.ca2_set_spatial_variant(-1) == lib.CA2_ERR_INVALID_ARG

@@ -67,6 +67,44 @@ def test_temporal_parity_small(ca2, name, sh, writes, n):
     check_close(to_host(out), ref, sh["dtype"], name)
 
 
+BF16_TEMPORAL = [c for c in TEMPORAL_CASES if c[1]["dtype"] == "bf16" and c[1]["d"] in (64, 72)]
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("name,sh,writes,n", BF16_TEMPORAL, ids=[c[0] for c in BF16_TEMPORAL])
+def test_temporal_parity_each_bf16_kernel(ca2, variant, name, sh, writes, n):
+    """The dimension-split VALU kernel (1) and the matrix-core rows (2), each
+    forced, against the oracle."""
+    cache, o = fill(ca2, sh, 100, writes)
+    q, k, v = (o.noisy(x, 1, 7, n) for x in ("q", "k", "v"))
+    out = empty_like_dev((sh["B"], n, sh["S"], sh["H"], sh["d"]), sh["dtype"])
+    ca2.ca2_set_temporal_variant(variant)
+    try:
+        cache.ca2_temporal_attn(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), out)
+    finally:
+        ca2.ca2_set_temporal_variant(0)
+    torch.cuda.synchronize()
+    ref = temporal_attn_ref(q, k, v, o.ring_k, o.ring_v, o.queue.slot_map(), o.scale)
+    check_close(to_host(out), ref, "bf16", f"{name} variant {variant}")
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+def test_temporal_ar_step_s256_full_each_kernel(ca2, variant):
+    """Both bf16 kernels at the 256-token shape, queue full, every output checked."""
+    sh = synth.WORKLOADS["ar_step_s256"]
+    cache, o = fill(ca2, sh, 7, [1, 8, 8, 8])
+    q, k, v = (o.noisy(x, 4, 50, 8) for x in ("q", "k", "v"))
+    out = empty_like_dev(q.shape, "bf16")
+    ca2.ca2_set_temporal_variant(variant)
+    try:
+        cache.ca2_temporal_attn(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), out)
+    finally:
+        ca2.ca2_set_temporal_variant(0)
+    torch.cuda.synchronize()
+    ref = temporal_attn_ref(q, k, v, o.ring_k, o.ring_v, o.queue.slot_map(), o.scale)
+    check_close(to_host(out), ref, "bf16", f"ar_step_s256 temporal variant {variant}")
+
+
 def test_temporal_ar_step_s256_full(ca2):
     """One denoising call at the 256-token shape, queue full (P_k = 25), every output checked."""
     sh = synth.WORKLOADS["ar_step_s256"]
