@@ -745,7 +745,12 @@ def traffic_summary(d, reps):
         return {k: sum(v[-reps:]) / len(v[-reps:]) for k, v in by.items()}, \
             next((r["Kernel_Name"] for r in rows if name in r["Kernel_Name"]), "")
 
-    out = {"method": traffic_summary.__doc__.split("\n\n")[0].replace("\n", " "), "kernels": {}}
+    # entries of (kernel, workload) pairs not counted in this directory are
+    # kept from the existing file (each carries the hash of the source it was
+    # counted on, so a stale one is recognised and not reported)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    old = json.load(open(path))["kernels"] if os.path.exists(path) else {}
+    out = {"method": traffic_summary.__doc__.split("\n\n")[0].replace("\n", " "), "kernels": dict(old)}
     for entry in sorted(os.listdir(d)):
         if not entry.startswith("rd_") or entry.endswith(".log"):
             continue
@@ -765,7 +770,8 @@ def traffic_summary(d, reps):
             "hbm_bytes_per_launch": round(read + write), "algorithmic_bytes": alg,
             "ratio_to_algorithmic": round((read + write) / alg, 3),
             "source": src, "source_sha256_16": source_hash(kernel)}
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+    out["kernels"] = dict(sorted(out["kernels"].items()))
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
     return out
 
