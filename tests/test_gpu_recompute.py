@@ -53,6 +53,26 @@ def test_bidirectional_temporal_parity(ca2, name, B, T, S, H, d, dtype):
     check_close(to_host(out), bidirectional_temporal_ref(q, k, v, d ** -0.5), dtype, name)
 
 
+MFMA_ROW_CASES = [c for c in FRAME_CASES if c[6] == "bf16" and c[5] in (64, 72)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("name,B,T,S,H,d,dtype", MFMA_ROW_CASES, ids=[c[0] for c in MFMA_ROW_CASES])
+def test_temporal_frames_matrix_core_rows(ca2, causal, name, B, T, S, H, d, dtype):
+    """The matrix-core temporal kernel, forced, on the cache-less forms (T up
+    to 16 runs it; longer T falls back to the dimension-split kernel)."""
+    q, k, v = frames_inputs(33, B, T, S, H, d, dtype)
+    out = empty_like_dev(q.shape, dtype)
+    ca2.ca2_set_temporal_variant(2)
+    try:
+        ca2.ca2_temporal_attn_frames(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), out, causal=causal)
+    finally:
+        ca2.ca2_set_temporal_variant(0)
+    torch.cuda.synchronize()
+    ref = causal_ref(q, k, v, d ** -0.5) if causal else bidirectional_temporal_ref(q, k, v, d ** -0.5)
+    check_close(to_host(out), ref, dtype, f"{name} causal={causal} variant 2")
+
+
 @pytest.mark.parametrize("name,B,T,S,H,d,dtype", FRAME_CASES, ids=IDS)
 def test_causal_temporal_frames_parity(ca2, name, B, T, S, H, d, dtype):
     q, k, v = frames_inputs(32, B, T, S, H, d, dtype)

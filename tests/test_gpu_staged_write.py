@@ -50,11 +50,22 @@ def _split(y, sh, n):
     return np.asarray(y).reshape(sh["B"], n, sh["S"], sh["H"], sh["d"])
 
 
-def test_staged_rollout_against_oracle(ca2):
+@pytest.mark.parametrize("temporal_variant", [0, 2])
+def test_staged_rollout_against_oracle(ca2, temporal_variant):
     """Conditioning frame, then 4 chunks of 4 (17 frames): the queue evicts,
     the 9 ring slots and the 9-entry TPE table both wrap. Each chunk: stage
     (ring + spatial), the write pass's temporal attention over the staged
-    frames, commit, then one denoising call on the committed cache."""
+    frames, commit, then one denoising call on the committed cache. Run with
+    the default temporal kernel and with the matrix-core rows forced (their
+    new keys then come from the ring's staging slots too)."""
+    ca2.ca2_set_temporal_variant(temporal_variant)
+    try:
+        _staged_rollout(ca2)
+    finally:
+        ca2.ca2_set_temporal_variant(0)
+
+
+def _staged_rollout(ca2):
     sh = SMALL
     B, S, H, d, l, P, Ps = sh["B"], sh["S"], sh["H"], sh["d"], sh["l"], sh["p_max"], sh["p_spatial"]
     scale = d ** -0.5
