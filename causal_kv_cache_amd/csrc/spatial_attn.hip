@@ -18,10 +18,11 @@
 //     PV product, fp32 accumulators. Where d % 16 == 8 (d = 72) the last
 //     16-dim QK step is half padding; there Q is multiplied by
 //     scale * log2 e once (rounded to bf16) and the padding carries the
-//     running maximum as one more product term (-m times a key entry of 1),
-//     so the product yields the shifted base-2 scores and P is exp2 of the
-//     MFMA output with no other per-score arithmetic. Elsewhere the scale
-//     and the maximum enter through one FMA per score;
+//     running maximum as three more product terms (-m split into three bf16
+//     parts, against key entries of 1), so the product yields the shifted
+//     base-2 scores and P is exp2 of the MFMA output with no other per-score
+//     arithmetic. Elsewhere the scale and the maximum enter through one FMA
+//     per score;
 //     the V row padding holds 1.0 at dim d, so row d of O^T is the softmax
 //     normaliser, computed by the MFMA from the same bf16 P as the numerator.
 // The fp32 path (for fp32 caches) is a plain LDS-tiled VALU kernel.
