@@ -315,7 +315,7 @@ def test_random_configs_both_kernels(ca2, name, sh, writes, n):
 
 
 @pytest.mark.parametrize("kernel,log2a", [("temporal", 52), ("spatial", 11)])
-@pytest.mark.parametrize("pattern", ["uniform", "tiered"])
+@pytest.mark.parametrize("pattern", ["uniform", "tiered", "late_max"])
 def test_large_negative_scores(ca2, pattern, kernel, log2a):
     """Inputs of magnitude 2^log2a (bf16-exact) with every score negative.
     Temporal at 2^52: every scaled score is about -1e32 in base 2, far below
@@ -326,7 +326,12 @@ def test_large_negative_scores(ca2, pattern, kernel, log2a):
     which cancels, as long as it cannot overflow: |scaled score| < 2^31).
     With equal keys the output is the mean of the cached values; with tiered
     keys it is the mean of the values of the least negative tier (one-hot up
-    to ties at these gaps); either way the oracle's."""
+    to ties at these gaps); either way the oracle's. late_max puts the new
+    frames' keys above every cached tier, so the maximum jumps by ~1e7 (base
+    2) when the last keys arrive: the raise must bring those keys' scores onto
+    the new maximum exactly alike (the spatial kernel re-scores the chunk with
+    the new maximum inside its product), and the output is the mean of the new
+    frames' values."""
     from oracle import TemporalQueue, SpatialCache
     B, H, d, S, l, P, Ps = 1, 2, 72, 64, 8, 8, 3
     sh = shape_of(B, H, d, S, l, P, Ps, "bf16")
@@ -334,7 +339,7 @@ def test_large_negative_scores(ca2, pattern, kernel, log2a):
     g = np.random.default_rng(7)
     ones = np.ones((B, l, S, H, d), np.float32)
     tier = np.ones_like(ones)
-    if pattern == "tiered":
+    if pattern in ("tiered", "late_max"):
         tier *= (1.0 + (np.arange(l) % 4) / 4.0)[None, :, None, None, None]   # 1, 1.25, 1.5, 1.75
     k_clean = (-a * tier).astype(np.float32)
     v_clean = synth.round_to_bf16(g.standard_normal(ones.shape).astype(np.float32))
@@ -342,7 +347,8 @@ def test_large_negative_scores(ca2, pattern, kernel, log2a):
     kd, vd = to_dev(k_clean, "bf16"), to_dev(v_clean, "bf16")
     cache.ca2_cache_write(kd, vd, kd, vd)
     q = (a * ones).astype(np.float32)
-    k_new = (-2.0 * a * ones).astype(np.float32)          # below every cached tier
+    # below every cached tier, or (late_max) above them all
+    k_new = ((-0.5 if pattern == "late_max" else -2.0) * a * ones).astype(np.float32)
     v_new = synth.round_to_bf16(g.standard_normal(ones.shape).astype(np.float32))
     dq, dk, dv = (to_dev(x, "bf16") for x in (q, k_new, v_new))
     out = empty_like_dev(q.shape, "bf16")
