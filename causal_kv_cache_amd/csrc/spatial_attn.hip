@@ -691,6 +691,11 @@ __device__ __forceinline__ void count_barrier(int& bars) {
 template <int D, int kPF>
 __device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw, int blk0, int nblk, int bars) {
   static_assert(kPF % 2 == 0 && kPF >= 4, "register ring of whole key pairs");
+  // The temporal wavefronts set the pace of the shared barriers (the spatial
+  // wavefronts wait for them there), so their instructions take issue
+  // priority over the spatial wavefront on the same SIMD, which fills the
+  // gaps while they wait for memory (step 1.420 -> 1.373 ms on one box).
+  __builtin_amdgcn_s_setprio(2);
   using G = DsGeom<D>;
   constexpr int DW = G::DW, DPL = G::DPL, QPL = kDcQPL, QH = kDcQH, LPR = 4 * QH;
   const int lane = threadIdx.x & 63;

@@ -77,6 +77,33 @@ def test_denoise_call_matches_oracle(ca2, name, sh, writes, n, mode, expect_fuse
     cache.close()
 
 
+FALLBACK = [c for c in CASES if not c[5] and c[1]["d"] in (64, 72)]
+
+
+@pytest.mark.parametrize("name,sh,writes,n,mode,expect_fused", FALLBACK, ids=[c[0] for c in FALLBACK])
+def test_denoise_call_fallback_with_matrix_core_temporal(ca2, name, sh, writes, n, mode, expect_fused):
+    """The two-launch fall-back with the matrix-core temporal kernel forced:
+    the temporal half follows the forced kernel, against the oracle."""
+    cache, o = _filled(ca2, sh, 901, writes)
+    qs, ks, vs = (o.noisy(x, 4, 1, n) for x in ("q", "k", "v"))
+    qt, kt, vt = (o.noisy(x, 4, 2, n) for x in ("q", "k", "v"))
+    dev = [to_dev(x, "bf16") for x in (qs, ks, vs, qt, kt, vt)]
+    out_s = empty_like_dev(qs.shape, "bf16")
+    out_t = empty_like_dev(qs.shape, "bf16")
+    ca2.ca2_set_temporal_variant(2)
+    try:
+        fused = cache.ca2_denoise_attn(*dev[:3], out_s, *dev[3:], out_t, mode=mode)
+    finally:
+        ca2.ca2_set_temporal_variant(0)
+    torch.cuda.synchronize()
+    assert not fused
+    check_close(to_host(out_s), o.spatial_out(qs, ks, vs, "prefix" if mode == 0 else "self"), "bf16",
+                f"{name} spatial")
+    ref_t = temporal_attn_ref(qt, kt, vt, o.ring_k, o.ring_v, o.queue.slot_map(), o.scale)
+    check_close(to_host(out_t), ref_t, "bf16", f"{name} temporal (matrix-core rows)")
+    cache.close()
+
+
 def test_denoise_call_staged_frames(ca2):
     """Write pass on a cache with staging slots: the temporal half reads the
     chunk's frames from their ring slots (k_t = v_t = NULL), the spatial half
