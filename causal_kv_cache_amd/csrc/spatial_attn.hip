@@ -714,16 +714,21 @@ __device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw,
   // every query of the row is served here (n <= QPL * QH), so the keys are
   // all k_total of them; query i stops at key p_k + i (causal)
   const int ke = k_total;
+  const float c = a.scale_log2e;
   bool first = true;
 
   for (int blk = blk0; blk < blk0 + nblk; ++blk) {
-    const int row = (blk * kDcTW + tw) * kDcRows + ri;
-    const bool row_ok = row < a.rows_total;
-    const int b = row_ok ? row / rpb : 0;
-    const int rr = row_ok ? row % rpb : 0;
-    const int64_t row_bytes = (int64_t)rr * D * 2;
+    // Addresses: a wavefront-uniform frame base plus a per-lane 32-bit offset
+    // within the frame (the rows of a wavefront lie in one batch: the launch
+    // checks rows_per_batch % kDcRows == 0 and frames under 4 GiB). Rows past
+    // the end are clamped to the last row: loaded, never stored.
+    const int row0 = (blk * kDcTW + tw) * kDcRows;
+    const bool row_ok = row0 + ri < a.rows_total;
+    const int rc = min(row0 + ri, a.rows_total - 1);
+    const int b = min(row0, a.rows_total - 1) / rpb;
+    const uint32_t lrow = (uint32_t)(rc - b * rpb) * (D * 2);
+    const uint32_t o16 = lrow + 16 * g, o4 = lrow + 64 * G::FULL + 4 * g;
     Slice<D> qs[QPL];
-    bool qok[QPL];
     int last_key[QPL];
     // every load is unconditional, indices clamped into range (as in the
     // stand-alone temporal kernel: the compiler's wait counts then keep the
@@ -731,31 +736,31 @@ __device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw,
 #pragma unroll
     for (int qq = 0; qq < QPL; ++qq) {
       const int qi = qg * QPL + qq;
-      qok[qq] = row_ok && qi < a.n;
-      last_key[qq] = !qok[qq] ? -1 : a.causal ? a.p_k + qi : k_total - 1;
-      load_slice<D>(qs[qq], qb + ((int64_t)b * a.n + min(qi, a.n - 1)) * frame_bytes + row_bytes, g);
+      last_key[qq] = !(row_ok && qi < a.n) ? -1 : a.p_k + qi;
+      const int64_t fo = ((int64_t)b * a.n + min(qi, a.n - 1)) * frame_bytes;
+      load_slice_at<D>(qs[qq], qb + fo, o16, o4);
     }
-    auto key_row = [&](int j, const unsigned char* ring, const unsigned char* fresh) -> const unsigned char* {
-      if (j < a.ring_keys) {
-        int slot = a.head + j;
-        if (slot >= a.p_max) slot -= a.p_max;
-        return ring + ((int64_t)b * a.p_max + slot) * frame_bytes + row_bytes;
-      }
-      return fresh + ((int64_t)b * a.n + (j - a.p_k)) * frame_bytes + row_bytes;
-    };
-    float m[QPL], l[QPL], acc[QPL][DPL];
+    float m[QPL], thr[QPL], l[QPL], acc[QPL][DPL];
 #pragma unroll
     for (int qq = 0; qq < QPL; ++qq) {
       m[qq] = kNoMax;
+      thr[qq] = kNoMax;
       l[qq] = 0.f;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[qq][e] = 0.f;
     }
     Slice<D> kr[kPF], vr[kPF];
+    // keys past the end read the last key again (finite values; their scores
+    // are masked to -inf, so they add exactly 0)
     auto refill = [&](int u, int jn) {
       const int jc = jn < ke ? jn : ke - 1;
-      load_slice<D>(kr[u], key_row(jc, rkb, knb), g);
-      load_slice<D>(vr[u], key_row(jc, rvb, vnb), g);
+      const bool queued = jc < a.ring_keys;
+      int slot = a.head + jc;
+      if (slot >= a.p_max) slot -= a.p_max;
+      const int64_t fo = queued ? ((int64_t)b * a.p_max + slot) * frame_bytes
+                                : ((int64_t)b * a.n + (jc - a.p_k)) * frame_bytes;
+      load_slice_at<D>(kr[u], (queued ? rkb : knb) + fo, o16, o4);
+      load_slice_at<D>(vr[u], (queued ? rvb : vnb) + fo, o16, o4);
     };
 #pragma unroll
     for (int u = 0; u < kPF; ++u) refill(u, u);
@@ -764,9 +769,11 @@ __device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw,
       first = false;
     }
     // one key pair: scores, lazy rescale, P rounded to bf16, O += P V by bf16
-    // dot products over the two keys (as the stand-alone temporal kernel)
-    auto process2 = [&](int j, const Slice<D>& k0, const Slice<D>& v0, const Slice<D>& k1, const Slice<D>& v1,
-                        bool two) {
+    // dot products over the two keys (as the stand-alone temporal kernel).
+    // Pairs of queued keys, which every query sees, skip the mask (a lane
+    // with no query then computes on clamped rows and stores nothing).
+    auto process2 = [&](int j, const Slice<D>& k0, const Slice<D>& v0, const Slice<D>& k1, const Slice<D>& v1) {
+      const bool mask = j + 1 >= a.p_k;              // wavefront-uniform
       float x0[QPL], x1[QPL];
       bool raise = false;
 #pragma unroll
@@ -779,11 +786,13 @@ __device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw,
           s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, qs[qq].w[x]),
                                                __builtin_bit_cast(bf16x2v, k1.w[x]), s1, false);
         }
-        s0 = quad_sum(s0);
-        s1 = quad_sum(s1);
-        x0[qq] = (j <= last_key[qq]) ? s0 * a.scale_log2e : -INFINITY;
-        x1[qq] = (two && j + 1 <= last_key[qq]) ? s1 * a.scale_log2e : -INFINITY;
-        raise |= fmaxf(x0[qq], x1[qq]) > m[qq] + kLazy;
+        x0[qq] = quad_sum(s0) * c;
+        x1[qq] = quad_sum(s1) * c;
+        if (mask) {
+          if (j > last_key[qq]) x0[qq] = -INFINITY;
+          if (j + 1 > last_key[qq]) x1[qq] = -INFINITY;
+        }
+        raise |= (x0[qq] > thr[qq]) | (x1[qq] > thr[qq]);
       }
       if (raise) {
 #pragma unroll
@@ -791,6 +800,7 @@ __device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw,
           const float mn = fmaxf(m[qq], fmaxf(x0[qq], x1[qq]));
           const float corr = fast_exp2(m[qq] - mn);
           m[qq] = mn;
+          thr[qq] = mn + kLazy;
           l[qq] *= corr;
 #pragma unroll
           for (int e = 0; e < DPL; ++e) acc[qq][e] *= corr;
@@ -799,9 +809,8 @@ __device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw,
       uint32_t vp[DPL];
 #pragma unroll
       for (int x = 0; x < DW; ++x) {
-        const uint32_t hi = two ? v1.w[x] : 0u;
-        vp[2 * x] = __builtin_amdgcn_perm(hi, v0.w[x], 0x05040100u);       // low halves
-        vp[2 * x + 1] = __builtin_amdgcn_perm(hi, v0.w[x], 0x07060302u);   // high halves
+        vp[2 * x] = __builtin_amdgcn_perm(v1.w[x], v0.w[x], 0x05040100u);       // low halves
+        vp[2 * x + 1] = __builtin_amdgcn_perm(v1.w[x], v0.w[x], 0x07060302u);   // high halves
       }
 #pragma unroll
       for (int qq = 0; qq < QPL; ++qq) {
@@ -816,7 +825,7 @@ __device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw,
     for (int j = 0; j < ke; j += kPF) {              // bounds are uniform per wavefront
 #pragma unroll
       for (int u = 0; u < kPF; u += 2) {             // ring slots are compile-time constants
-        process2(j + u, kr[u], vr[u], kr[u + 1], vr[u + 1], j + u + 1 < ke);   // masked past ke
+        process2(j + u, kr[u], vr[u], kr[u + 1], vr[u + 1]);
         refill(u, j + u + kPF);
         refill(u + 1, j + u + 1 + kPF);
         count_barrier(bars);
@@ -824,13 +833,13 @@ __device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw,
     }
 #pragma unroll
     for (int qq = 0; qq < QPL; ++qq) {
-      if (!qok[qq]) continue;
+      if (last_key[qq] < 0) continue;
       const int qi = qg * QPL + qq;
       const float inv = 1.f / l[qq];
       float o[DPL];
 #pragma unroll
       for (int e = 0; e < DPL; ++e) o[e] = acc[qq][e] * inv;
-      store_slice<D>(ob + ((int64_t)b * a.n + qi) * frame_bytes + row_bytes, g, o);
+      store_slice<D>(ob + ((int64_t)b * a.n + qi) * frame_bytes + lrow, g, o);
     }
   }
   if (first) count_barrier(bars);
@@ -1002,6 +1011,9 @@ bool denoise_call_fusable(int dtype, int d, const SpatialArgs& sa, const Tempora
   if (dtype != 1 || (d != 64 && d != 72)) return false;                // the bf16 MFMA path, 2 waves per SIMD
   if (sa.tokens % kBN != 0 || ta.n > kDcQH * kDcQPL || !ta.causal) return false;
   if (g_forced_variant.load(std::memory_order_relaxed) != 0) return false;   // a forced spatial variant wins
+  // the temporal wavefronts' addressing: the rows of a wavefront in one
+  // batch, per-lane 32-bit offsets within a frame
+  if (ta.rows_per_batch % kDcRows != 0 || (int64_t)ta.rows_per_batch * d * 2 > 0xFFFFFFFFll) return false;
   const int64_t nwg = (int64_t)((sa.tokens + 127) / 128) * sa.n * sa.heads * sa.batch;
   return nwg <= device_cus();                                          // one round of workgroups
 }

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(64 * kWaves) void temporal_attn_kernel(TemporalArgs
   __shared__ uint4 lds[C::LDS_U4];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: key ranges, branches
   const int row0 = blockIdx.x * ROWS;
   const int ri = lane / QL;
   const int q0 = blockIdx.y * QL;           // first query frame of this block
@@ -291,7 +291,10 @@ __global__ __launch_bounds__(64 * kWaves) void temporal_attn_kernel(TemporalArgs
 
 constexpr int kQPL = 4;              // queries per lane
 
-template <int D, int QH>
+// U: the workgroup's rows lie in one batch and a frame is under 4 GiB
+// (checked at launch), so a key's address is a wavefront-uniform frame base
+// plus per-lane 32-bit offsets (no vector address arithmetic per key).
+template <int D, int QH, bool U>
 __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, int splits) {
   using G = DsGeom<D>;
   constexpr int DW = G::DW, DPL = G::DPL;
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
   extern __shared__ float merge_lds[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: key ranges, branches
   const int g = lane & 3;                          // dimension group
   const int qg = (lane >> 2) % QH;                 // query group
   const int ri = lane / LPR;
@@ -308,10 +311,12 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
   const int row = blockIdx.x * ROWS + ri;
   const bool row_ok = row < a.rows_total;
   const int rpb = a.rows_per_batch;
-  const int b = row_ok ? row / rpb : 0;
-  const int rr = row_ok ? row % rpb : 0;
+  const int b = U ? min(blockIdx.x * ROWS, a.rows_total - 1) / rpb : row_ok ? row / rpb : 0;
+  const int rr = U ? min(row, a.rows_total - 1) - b * rpb : row_ok ? row % rpb : 0;
   const int64_t row_bytes = (int64_t)rr * D * 2;
   const int64_t frame_bytes = (int64_t)rpb * D * 2;
+  const uint32_t o16 = (uint32_t)row_bytes + 16 * g;                    // (U)
+  const uint32_t o4 = (uint32_t)row_bytes + 64 * G::FULL + 4 * g;
 
   const unsigned char* qb = static_cast<const unsigned char*>(a.q);
   const unsigned char* knb = static_cast<const unsigned char*>(a.k_new);
@@ -330,7 +335,8 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
     qok[qq] = row_ok && qi < a.n;
     last_key[qq] = !qok[qq] ? -1 : a.causal ? a.p_k + qi : k_total - 1;
     if (qok[qq]) {
-      load_slice<D>(qs[qq], qb + ((int64_t)b * a.n + qi) * frame_bytes + row_bytes, g);
+      if (U) load_slice_at<D>(qs[qq], qb + ((int64_t)b * a.n + qi) * frame_bytes, o16, o4);
+      else load_slice<D>(qs[qq], qb + ((int64_t)b * a.n + qi) * frame_bytes + row_bytes, g);
     } else {
 #pragma unroll
       for (int w = 0; w < DW; ++w) qs[qq].w[w] = 0u;
@@ -352,34 +358,53 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
     return fresh + ((int64_t)b * a.n + (j - a.p_k)) * frame_bytes + row_bytes;
   };
 
-  float m[kQPL], l[kQPL], acc[kQPL][DPL];
-#pragma unroll
-  for (int qq = 0; qq < kQPL; ++qq) {
-    m[qq] = kNoMax;
-    l[qq] = 0.f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[qq][e] = 0.f;
-  }
-
   // K/V slices of keys j .. j+3 in a 4-slot register ring, consumed in pairs:
   // while the pair (j, j+1) is processed the pair (j+2, j+3) is in flight,
   // and the slots of (j, j+1) are refilled with (j+4, j+5) right after.
   constexpr int kPF = 4;
   Slice<D> kr[kPF], vr[kPF];
-#pragma unroll
-  for (int u = 0; u < kPF; ++u)
-    if (row_ok && kb + u < ke) {
-      load_slice<D>(kr[u], key_row(kb + u, rkb, knb), g);
-      load_slice<D>(vr[u], key_row(kb + u, rvb, vnb), g);
+  // K and V of key jn into ring slot u, if jn is in the range (U: the queue
+  // or the new frames by a uniform select, the same per-lane offsets for both)
+  auto refill = [&](int u, int jn) {
+    if (jn >= ke) return;
+    if constexpr (U) {
+      const bool queued = jn < a.ring_keys;
+      int slot = a.head + jn;
+      if (slot >= a.p_max) slot -= a.p_max;
+      const int64_t fo = queued ? ((int64_t)b * a.p_max + slot) * frame_bytes
+                                : ((int64_t)b * a.n + (jn - a.p_k)) * frame_bytes;
+      load_slice_at<D>(kr[u], (queued ? rkb : knb) + fo, o16, o4);
+      load_slice_at<D>(vr[u], (queued ? rvb : vnb) + fo, o16, o4);
+    } else if (row_ok) {
+      load_slice<D>(kr[u], key_row(jn, rkb, knb), g);
+      load_slice<D>(vr[u], key_row(jn, rvb, vnb), g);
     }
+  };
+
+  float m[kQPL], thr[kQPL], l[kQPL], acc[kQPL][DPL];
+#pragma unroll
+  for (int qq = 0; qq < kQPL; ++qq) {
+    m[qq] = kNoMax;
+    thr[qq] = kNoMax;
+    l[qq] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[qq][e] = 0.f;
+  }
+
+#pragma unroll
+  for (int u = 0; u < kPF; ++u) refill(u, kb + u);
   // One key pair: scores, lazy rescale, then P of the pair rounded to bf16 and
   // O += P V as bf16 dot products over the two keys (one v_dot2 per dimension
   // and query; the row sum is the same dot product with (1, 1), so numerator
   // and normaliser use the same rounded P). `two` (wavefront-uniform) is false
   // when key j+1 is past the range: its score is -inf and its V words are
-  // zeroed, so a stale slot cannot turn 0 * V into NaN.
+  // zeroed, so a stale slot cannot turn 0 * V into NaN. Pairs of keys that
+  // every query of the range sees (queued keys, both within the range) skip
+  // the mask.
+  const int unmasked_end = min(a.p_k, ke);
   auto process2 = [&](int j, const Slice<D>& k0, const Slice<D>& v0, const Slice<D>& k1, const Slice<D>& v1,
                       bool two) {
+    const bool mask = j + 1 >= unmasked_end;       // wavefront-uniform
     float x0[kQPL], x1[kQPL];
     bool raise = false;
 #pragma unroll
@@ -392,11 +417,13 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
         s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, qs[qq].w[w]),
                                              __builtin_bit_cast(bf16x2v, k1.w[w]), s1, false);
       }
-      s0 = quad_sum(s0);
-      s1 = quad_sum(s1);
-      x0[qq] = (j <= last_key[qq]) ? s0 * a.scale_log2e : -INFINITY;
-      x1[qq] = (two && j + 1 <= last_key[qq]) ? s1 * a.scale_log2e : -INFINITY;
-      raise |= fmaxf(x0[qq], x1[qq]) > m[qq] + kLazy;
+      x0[qq] = quad_sum(s0) * a.scale_log2e;
+      x1[qq] = quad_sum(s1) * a.scale_log2e;
+      if (mask) {
+        if (j > last_key[qq]) x0[qq] = -INFINITY;
+        if (!two || j + 1 > last_key[qq]) x1[qq] = -INFINITY;
+      }
+      raise |= (x0[qq] > thr[qq]) | (x1[qq] > thr[qq]);
     }
     if (raise) {
 #pragma unroll
@@ -404,6 +431,7 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
         const float mn = fmaxf(m[qq], fmaxf(x0[qq], x1[qq]));
         const float corr = fast_exp2(m[qq] - mn);
         m[qq] = mn;
+        thr[qq] = mn + kLazy;
         l[qq] *= corr;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) acc[qq][e] *= corr;
@@ -424,12 +452,6 @@ __global__ __launch_bounds__(256) void temporal_attn_ds_kernel(TemporalArgs a, i
 #pragma unroll
       for (int e = 0; e < DPL; ++e)
         acc[qq][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2v, vp[e]), acc[qq][e], false);
-    }
-  };
-  auto refill = [&](int u, int jn) {
-    if (row_ok && jn < ke) {
-      load_slice<D>(kr[u], key_row(jn, rkb, knb), g);
-      load_slice<D>(vr[u], key_row(jn, rvb, vnb), g);
     }
   };
   for (int j = kb; j < ke; j += kPF) {                   // bounds are uniform per wavefront
@@ -503,7 +525,11 @@ hipError_t launch_ds_q(const TemporalArgs& a, hipStream_t s) {
   const int k_min = a.causal ? a.p_k + (a.n < QB ? a.n : QB) : a.p_k + a.n;   // fewest keys of a block
   if (splits > k_min) splits = k_min;
   const size_t lds = splits > 1 ? (size_t)(splits - 1) * 64 * kQPL * (DsGeom<D>::DPL + 2) * sizeof(float) : 0;
-  hipLaunchKernelGGL((temporal_attn_ds_kernel<D, QH>), dim3(groups, qblocks), dim3(64 * splits), lds, s, a, splits);
+  const int64_t frame_bytes = (int64_t)a.rows_per_batch * D * 2;
+  if (a.rows_per_batch % ROWS == 0 && frame_bytes <= 0xFFFFFFFFll)
+    hipLaunchKernelGGL((temporal_attn_ds_kernel<D, QH, true>), dim3(groups, qblocks), dim3(64 * splits), lds, s, a, splits);
+  else
+    hipLaunchKernelGGL((temporal_attn_ds_kernel<D, QH, false>), dim3(groups, qblocks), dim3(64 * splits), lds, s, a, splits);
   return hipGetLastError();
 }
 

@@ -41,6 +41,25 @@ __device__ __forceinline__ void load_slice(Slice<D>& s, const unsigned char* row
     s.w[4 * G::FULL + r] = *reinterpret_cast<const uint32_t*>(row + 16 * (4 * G::FULL + r) + 4 * g);
 }
 
+// The same slice from a wavefront-uniform base plus per-lane 32-bit offsets:
+// off16 = the row's offset + 16 g (whole chunks, the rest as immediates),
+// off4 = the row's offset + the leftover chunk's start + 4 g. The addresses
+// take the scalar-base form of the global loads, so a key costs no vector
+// address arithmetic.
+template <int D>
+__device__ __forceinline__ void load_slice_at(Slice<D>& s, const unsigned char* base, uint32_t off16, uint32_t off4) {
+  using G = DsGeom<D>;
+  const unsigned char* p16 = base + off16;
+#pragma unroll
+  for (int c = 0; c < G::FULL; ++c) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p16 + 64 * c);
+    s.w[4 * c + 0] = u.x; s.w[4 * c + 1] = u.y; s.w[4 * c + 2] = u.z; s.w[4 * c + 3] = u.w;
+  }
+  const unsigned char* p4 = base + off4;
+#pragma unroll
+  for (int r = 0; r < G::REM; ++r) s.w[4 * G::FULL + r] = *reinterpret_cast<const uint32_t*>(p4 + 16 * r);
+}
+
 template <int D>
 __device__ __forceinline__ void store_slice(unsigned char* row, int g, const float* v) {
   using G = DsGeom<D>;
