@@ -825,6 +825,7 @@ __device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw,
     for (int j = 0; j < ke; j += kPF) {              // bounds are uniform per wavefront
 #pragma unroll
       for (int u = 0; u < kPF; u += 2) {             // ring slots are compile-time constants
+        if (j + u >= ke) break;                      // no pair left (uniform)
         process2(j + u, kr[u], vr[u], kr[u + 1], vr[u + 1]);
         refill(u, j + u + kPF);
         refill(u + 1, j + u + 1 + kPF);
