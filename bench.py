@@ -317,13 +317,22 @@ SOURCES = {"spatial_prefix": "spatial_attn.hip", "spatial_self": "spatial_attn.h
 
 
 def source_hash(kernel):
-    """Hash of the kernel's source code and the device headers it includes,
-    with comments and whitespace removed (a comment edit does not invalidate
-    recorded counters)."""
+    """Hash of the kernel's source file and the library headers it includes
+    (directly or through other headers), with comments and whitespace removed
+    (a comment edit does not invalidate recorded counters)."""
     import re
+    csrc = os.path.join(ROOT, "causal_kv_cache_amd", "csrc")
+    names, todo = [], [SOURCES[kernel]]
+    while todo:
+        name = todo.pop(0)
+        if name in names or not os.path.exists(os.path.join(csrc, name)):
+            continue
+        names.append(name)
+        with open(os.path.join(csrc, name)) as f:
+            todo += re.findall(r'#include\s+"([^"]+)"', f.read())
     src = ""
-    for name in (SOURCES[kernel], "device_common.hpp", "temporal_common.hpp"):
-        with open(os.path.join(ROOT, "causal_kv_cache_amd", "csrc", name)) as f:
+    for name in names:
+        with open(os.path.join(csrc, name)) as f:
             src += f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
