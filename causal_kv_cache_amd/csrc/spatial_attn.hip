@@ -750,8 +750,8 @@ __device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw,
       for (int e = 0; e < DPL; ++e) acc[qq][e] = 0.f;
     }
     Slice<D> kr[kPF], vr[kPF];
-    // keys past the end read the last key again (finite values; their scores
-    // are masked to -inf, so they add exactly 0)
+    // keys past the end read the last key again; their scores are masked to
+    // -inf, so their P is exactly 0 (and the slot never holds stale data)
     auto refill = [&](int u, int jn) {
       const int jc = jn < ke ? jn : ke - 1;
       const bool queued = jc < a.ring_keys;

@@ -287,7 +287,9 @@ __global__ __launch_bounds__(64 * kWaves) void temporal_attn_kernel(TemporalArgs
 // 2^8 (base-2 units), so the accumulators are rescaled a handful of times per
 // row instead of once per key.
 // When rows are few, the key range is split over up to 4 wavefronts of a
-// workgroup and the partial results are merged through LDS.
+// workgroup and the partial results are merged through LDS. Pairs of queued
+// keys skip the causal mask (every query sees them), and the raise test is
+// two compares against a threshold kept beside the maximum.
 
 constexpr int kQPL = 4;              // queries per lane
 
