@@ -764,7 +764,10 @@ __device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw,
     };
 #pragma unroll
     for (int u = 0; u < kPF; ++u) refill(u, u);
-    if (first) {           // the first barrier once the first keys are in flight
+    // The first barrier once the first keys are in flight. It also fences the
+    // compiler's scheduling: with the ring loads free to move into the loop,
+    // its wait counts fall back to waiting for every load in each pair.
+    if (first) {
       count_barrier(bars);
       first = false;
     }
