@@ -124,7 +124,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();                  // k-tile t visible; stage of k-tile t-1 free
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    if (t + 1 < KT) issue(t + 1);
+    // A copy instruction holds its wavefront while the memory pipeline takes
+    // it, so the next k-tile's copies are issued at two times: by waves 0-3
+    // right after the barrier and by waves 4-7 after their first k-step.
+    // Waves are dealt to the SIMDs in turn, so waves w and w + 4 share one and
+    // each SIMD has one wavefront running MFMAs while the other issues copies.
+    if (t + 1 < KT && wave < 4) issue(t + 1);
     const unsigned char* sw = smem + (t % kStages) * STAGE;
     load_ops(sw, 0, 0);
 #pragma unroll
@@ -139,6 +144,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[s & 1][i], xb[s & 1][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
+      if (s == 0 && t + 1 < KT && wave >= 4) issue(t + 1);
     }
   }
 
