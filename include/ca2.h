@@ -210,7 +210,8 @@ ca2_status ca2_spatial_attn(const ca2_cache* cache, const void* q, const void* k
  * temporal wavefronts share every SIMD.
  * Fused when: bf16 cache, head_dim 64 or 72, tokens a multiple of 64,
  * n_frames <= 8, the spatial work fits the chip's compute units in one round
- * (ceil(tokens/128) * n * heads * batch workgroups), and no spatial launch
+ * (ceil(tokens/128) * n * heads * batch workgroups), one frame of K or V
+ * (tokens * heads * head_dim * 2 bytes) under 4 GiB, and no spatial launch
  * variant is forced (ca2_set_spatial_variant). Otherwise the two kernels
  * run back to back on `stream`. *fused (may be NULL) is set to 1 or 0.
  */
