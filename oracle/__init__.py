@@ -20,7 +20,9 @@ cites the passage of the source pages it follows. The pages are:
 * "Ca2-VDM summary" -- atlas.scime.ai summary (Approach, Key results).
 
 Pin status of each function is stated in its docstring and collected in the
-design notes; "parity unpinned" marks a reading the pages do not fix.
+design notes. Where the pages leave a step open, the reading taken is named
+in the docstring, and the function is pinned for that reading by a closed
+form or a construction other than its own.
 """
 from .attention import (
     softmax_rows,

@@ -75,8 +75,15 @@ class SpatialCache:
     an empty slot if one exists (lowest index first), else the slot of the
     oldest frame held. Logical order is oldest to newest. While fewer than P'
     clean frames exist, the logical list is left-padded by repeating the oldest
-    frame held (reading taken for the pages' silence; parity unpinned by the
-    pages, modelled on the self-repeat alignment of key design 3).
+    frame held (a reading: the pages are silent on this case; it keeps the
+    (P'+1)S keys of key design 3, modelled on its self-repeat alignment).
+
+    Pinned by hand-written logical lists per write sequence and, for the
+    padding, by the closed form that attention over a prefix repeating a
+    frame m times equals attention over the distinct frames with that frame's
+    exponentials counted m times (hand-written multiplicities, loop-evaluated
+    weighted softmax); padding with the newest frame, with the target frame,
+    with zeros, or not at all each fails it.
     """
 
     def __init__(self, p_spatial: int):

@@ -20,9 +20,13 @@ Block = spatial attention (prefix-enhanced for targets, self for clean frames)
 frame's own timestep embedding (adaLN style: shift and scale).
 
 The layer forms (layer norm, tanh-GELU, sinusoidal timestep embedding,
-shift/scale modulation) are textbook choices: the pages do not specify the
-backbone, so those definitions are parity unpinned; the two cache properties
-above are what the tests pin.
+shift/scale modulation) are textbook choices, since the pages do not specify
+the backbone. Each is pinned by what its mathematics fixes (zero mean and the
+epsilon-shrunk variance of layer norm, the odd-part identity and erf bound of
+tanh-GELU, the values and frequencies of the embedding, the closed-form
+roles of the modulation vectors), with planted mistakes that fail those
+pins; the two cache properties above are pinned by the invariance and
+full-recompute checks.
 """
 from __future__ import annotations
 
