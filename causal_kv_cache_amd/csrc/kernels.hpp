@@ -130,6 +130,7 @@ void set_spatial_variant(int v);
 // Process-wide kernel choice for bf16 temporal attention (0 and 1 =
 // dimension-split VALU kernel, 2 = matrix-core rows where n <= 16).
 void set_temporal_variant(int v);
+int temporal_variant();
 
 bool temporal_supported(int dtype, int head_dim);
 bool spatial_supported(int dtype, int head_dim);

@@ -29,6 +29,7 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "temporal_common.hpp"
+#include "temporal_mfma.hpp"
 
 #include <atomic>
 #include <cstdlib>
@@ -852,9 +853,11 @@ __device__ __forceinline__ void temporal_lockstep(const TemporalArgs& a, int tw,
 
 // Wavefronts 0..3: spatial work item w (4 x 32 queries, whole 64-key tiles,
 // copies issued by the computing wavefronts); wavefronts 4..4+kDcTW-1:
-// temporal row blocks [blockIdx.x * nblk, +nblk). Launched only when the
-// spatial grid fits on the chip in one round (one workgroup per CU).
-template <int D, int kStages, int kPF>
+// temporal row blocks [blockIdx.x * nblk, +nblk), by the dimension-split
+// lockstep loop or, with kTm (the forced matrix-core temporal variant, slower
+// here too), by the matrix-core rows over the same rows. Launched only when
+// the spatial grid fits on the chip in one round (one workgroup per CU).
+template <int D, int kStages, int kPF, bool kTm>
 __global__ __launch_bounds__(64 * (4 + kDcTW)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void denoise_call_kernel(SpatialArgs sa, TemporalArgs ta, int nblk) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * SCfg<D, 4>::STAGE];
@@ -863,7 +866,17 @@ void denoise_call_kernel(SpatialArgs sa, TemporalArgs ta, int nblk) {
     spatial_pipe<D, 1, 4, true, kStages, 1, false>(sa, xcd_work_index(blockIdx.x, gridDim.x), threadIdx.x, smem);
   } else {
     const int n_tiles = (1 + sa.n_prefix) * (sa.tokens / kBN);   // the spatial wavefronts' barrier count
-    temporal_lockstep<D, kPF>(ta, wave - 4, blockIdx.x * nblk, nblk, n_tiles);
+    if constexpr (kTm) {
+      __builtin_amdgcn_s_setprio(2);
+      const int tw = wave - 4;
+      auto row_of = [&](int i) { return ((blockIdx.x * nblk + i / kDcRows) * kDcTW + tw) * kDcRows + i % kDcRows; };
+      int rows = 0;
+      for (int i = 0; i < nblk * kDcRows; ++i)
+        if (row_of(i) < ta.rows_total) rows = i + 1;
+      temporal_mfma_rows<D>(ta, row_of, rows, n_tiles);
+    } else {
+      temporal_lockstep<D, kPF>(ta, wave - 4, blockIdx.x * nblk, nblk, n_tiles);
+    }
   }
 }
 
@@ -1039,8 +1052,14 @@ hipError_t launch_denoise_call(int dtype, int d, const SpatialArgs& sa, const Te
   const int64_t blocks = ((int64_t)ta.rows_total + kDcBlockRows - 1) / kDcBlockRows;
   const int nblk = (int)((blocks + nwg - 1) / nwg);
   const dim3 grid((unsigned)nwg), block(64 * (4 + kDcTW));
-  if (d == 64) hipLaunchKernelGGL((denoise_call_kernel<64, 4, kDcRing>), grid, block, 0, s, sa, ta, nblk);
-  else hipLaunchKernelGGL((denoise_call_kernel<72, 4, kDcRing>), grid, block, 0, s, sa, ta, nblk);
+  const bool tm = temporal_variant() == 2;
+  if (d == 64) {
+    if (tm) hipLaunchKernelGGL((denoise_call_kernel<64, 4, kDcRing, true>), grid, block, 0, s, sa, ta, nblk);
+    else hipLaunchKernelGGL((denoise_call_kernel<64, 4, kDcRing, false>), grid, block, 0, s, sa, ta, nblk);
+  } else {
+    if (tm) hipLaunchKernelGGL((denoise_call_kernel<72, 4, kDcRing, true>), grid, block, 0, s, sa, ta, nblk);
+    else hipLaunchKernelGGL((denoise_call_kernel<72, 4, kDcRing, false>), grid, block, 0, s, sa, ta, nblk);
+  }
   return hipGetLastError();
 }
 

@@ -631,5 +631,6 @@ hipError_t launch_temporal(int dtype, int d, const TemporalArgs& a, hipStream_t 
 }
 
 void set_temporal_variant(int v) { g_forced_temporal.store(v, std::memory_order_relaxed); }
+int temporal_variant() { return g_forced_temporal.load(std::memory_order_relaxed); }
 
 }  // namespace ca2

@@ -392,7 +392,8 @@ ca2_status ca2_set_spatial_variant(int32_t variant);
 /*
  * Test and measurement switch: force the kernel of bf16 temporal attention
  * (ca2_temporal_attn, ca2_temporal_attn_frames, and the temporal half of
- * ca2_denoise_attn when it runs as two launches) for every later call in the
+ * ca2_denoise_attn, whether it runs as two launches or in the fused launch's
+ * temporal wavefronts) for every later call in the
  * process: 0 = the default (the dimension-split kernel: VALU dot products),
  * 1 = the same, 2 = matrix-core rows wherever they apply (n <= 16, head_dim
  * 64 or 72; slower, kept for comparison). Every choice computes the same

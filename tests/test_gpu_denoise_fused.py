@@ -77,6 +77,33 @@ def test_denoise_call_matches_oracle(ca2, name, sh, writes, n, mode, expect_fuse
     cache.close()
 
 
+FUSED = [c for c in CASES if c[5]]
+
+
+@pytest.mark.parametrize("name,sh,writes,n,mode,expect_fused", FUSED, ids=[c[0] for c in FUSED])
+def test_denoise_call_with_matrix_core_temporal(ca2, name, sh, writes, n, mode, expect_fused):
+    """The fused launch with the matrix-core temporal rows forced in its
+    temporal wavefronts, against the oracle; the spatial half is unchanged."""
+    cache, o = _filled(ca2, sh, 903, writes)
+    qs, ks, vs = (o.noisy(x, 5, 1, n) for x in ("q", "k", "v"))
+    qt, kt, vt = (o.noisy(x, 5, 2, n) for x in ("q", "k", "v"))
+    dev = [to_dev(x, "bf16") for x in (qs, ks, vs, qt, kt, vt)]
+    out_s = empty_like_dev(qs.shape, "bf16")
+    out_t = empty_like_dev(qs.shape, "bf16")
+    ca2.ca2_set_temporal_variant(2)
+    try:
+        fused = cache.ca2_denoise_attn(*dev[:3], out_s, *dev[3:], out_t, mode=mode)
+    finally:
+        ca2.ca2_set_temporal_variant(0)
+    torch.cuda.synchronize()
+    assert fused
+    check_close(to_host(out_s), o.spatial_out(qs, ks, vs, "prefix" if mode == 0 else "self"), "bf16",
+                f"{name} spatial")
+    ref_t = temporal_attn_ref(qt, kt, vt, o.ring_k, o.ring_v, o.queue.slot_map(), o.scale)
+    check_close(to_host(out_t), ref_t, "bf16", f"{name} temporal (matrix-core rows, fused)")
+    cache.close()
+
+
 FALLBACK = [c for c in CASES if not c[5] and c[1]["d"] in (64, 72)]
 
 
