@@ -788,7 +788,9 @@ def traffic_summary(d, reps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    # ~0.4 s of timed steps: long enough to average over clock and
+    # box-to-box jitter, short against the rest of the run
+    ap.add_argument("--steps", type=int, default=300)
     # untimed steps first: the clock ramps up over the first few ms of load,
     # and 3 warmup steps (~5 ms) left ~4 % of that ramp in the timed steps
     ap.add_argument("--warmup", type=int, default=30)
