@@ -104,6 +104,68 @@ def test_denoise_call_with_matrix_core_temporal(ca2, name, sh, writes, n, mode, 
     cache.close()
 
 
+def _random_fusable(n_cfg, seed):
+    """Seeded shapes inside the fused launch's domain (bf16, head_dim 64 or
+    72, whole 64-token tiles, n <= 8, the spatial grid within one round of 256
+    workgroups), with any chunk, queue length before and after eviction, a
+    wrapped ring, prefix size 0..l-1 and either spatial mode; the oracle's
+    spatial work is capped so the set runs in seconds."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n_cfg:
+        d = int(g.choice([64, 72]))
+        S = 64 * int(g.integers(1, 5))
+        B, H = int(g.integers(1, 3)), int(g.integers(1, 9))
+        l = int(g.integers(1, 17))
+        n = int(g.integers(1, min(l, 8) + 1))
+        p_max = int(g.integers(1, 50))
+        p_spatial = int(g.integers(0, min(l, 16)))
+        mode = int(g.integers(0, 2))
+        writes = [1] + [int(g.integers(1, l + 1)) for _ in range(int(g.integers(0, 2 * p_max // l + 3)))]
+        nwg = -(-S // 128) * n * H * B
+        if nwg > 256 or B * n * H * S * S * (p_spatial + 1) * d > 1.5e9:
+            continue
+        sh = shape_of(B, H, d, S, l, p_max, p_spatial, p_max + l + int(g.integers(0, 6)))
+        out.append((f"rand{len(out)}_d{d}_B{B}H{H}S{S}_l{l}P{p_max}p{p_spatial}_w{sum(writes)}_n{n}_m{mode}",
+                    sh, writes, n, mode))
+    return out
+
+
+RANDOM_FUSED = _random_fusable(24, 4242)
+
+
+@pytest.mark.parametrize("name,sh,writes,n,mode", RANDOM_FUSED, ids=[c[0] for c in RANDOM_FUSED])
+def test_denoise_call_random_shapes(ca2, name, sh, writes, n, mode):
+    """Seeded shapes through the fused launch, both temporal forms, against
+    the oracle; the spatial half bit-identical to the stand-alone kernel."""
+    cache, o = _filled(ca2, sh, 904, writes)
+    qs, ks, vs = (o.noisy(x, 6, 1, n) for x in ("q", "k", "v"))
+    qt, kt, vt = (o.noisy(x, 6, 2, n) for x in ("q", "k", "v"))
+    dev = [to_dev(x, "bf16") for x in (qs, ks, vs, qt, kt, vt)]
+    ref_s = o.spatial_out(qs, ks, vs, "prefix" if mode == 0 and sh["p_spatial"] > 0 else "self")
+    ref_t = temporal_attn_ref(qt, kt, vt, o.ring_k, o.ring_v, o.queue.slot_map(), o.scale)
+    solo = empty_like_dev(qs.shape, "bf16")
+    ca2.ca2_set_spatial_variant(1)
+    try:
+        cache.ca2_spatial_attn(*dev[:3], solo, mode=mode)
+    finally:
+        ca2.ca2_set_spatial_variant(0)
+    for tv in (0, 2):
+        out_s = empty_like_dev(qs.shape, "bf16")
+        out_t = empty_like_dev(qs.shape, "bf16")
+        ca2.ca2_set_temporal_variant(tv)
+        try:
+            fused = cache.ca2_denoise_attn(*dev[:3], out_s, *dev[3:], out_t, mode=mode)
+        finally:
+            ca2.ca2_set_temporal_variant(0)
+        torch.cuda.synchronize()
+        assert fused, f"{name}: expected the fused launch"
+        check_close(to_host(out_s), ref_s, "bf16", f"{name} spatial (temporal variant {tv})")
+        check_close(to_host(out_t), ref_t, "bf16", f"{name} temporal (variant {tv})")
+        assert torch.equal(solo, out_s), f"{name}: fused spatial half differs from the stand-alone kernel"
+    cache.close()
+
+
 FALLBACK = [c for c in CASES if not c[5] and c[1]["d"] in (64, 72)]
 
 
