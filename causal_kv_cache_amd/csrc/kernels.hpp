@@ -128,7 +128,9 @@ hipError_t launch_denoise_call(int dtype, int head_dim, const SpatialArgs& sa, c
 // Process-wide launch variant of the bf16 spatial kernel (0 = by size, 1..4).
 void set_spatial_variant(int v);
 // Process-wide kernel choice for bf16 temporal attention (0 and 1 =
-// dimension-split VALU kernel, 2 = matrix-core rows where n <= 16).
+// dimension-split VALU kernel, 2 = matrix-core rows where n <= 16), in the
+// stand-alone kernels and in the fused denoising launch's temporal
+// wavefronts alike; temporal_variant() reads it back.
 void set_temporal_variant(int v);
 int temporal_variant();
 
