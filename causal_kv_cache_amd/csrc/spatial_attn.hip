@@ -665,9 +665,8 @@ __global__ __launch_bounds__(64 * (kSW + PROD)) __attribute__((amdgpu_waves_per_
 // the temporal keys staged through LDS by the same copies as the spatial
 // tiles (4 copies per key pair instead of 12 lane-duplicated loads, 140
 // VGPRs), the same plus the spatial copy wavefront (9 wavefronts), and the
-// two halves as separate workgroups of one launch with no shared barriers.
-// Timing-only copies isolate the cost: the temporal loads alone add ~3.6 us
-// to the spatial half, its arithmetic alone ~2.8 us, both together ~9 us.
+// two halves as separate workgroups of one launch with no shared barriers;
+// the matrix-core temporal rows in the temporal wavefronts (kTm) are slower.
 // Rows of a temporal wavefront: 4 dimension groups x kDcQH query groups of
 // kDcQPL queries, so a row's 8 new frames are covered and 4 rows share a
 // wavefront; the key range is not split, so no partial results are merged.
