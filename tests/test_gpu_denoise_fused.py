@@ -193,10 +193,11 @@ def test_denoise_call_fallback_with_matrix_core_temporal(ca2, name, sh, writes, 
     cache.close()
 
 
-def test_denoise_call_staged_frames(ca2):
+@pytest.mark.parametrize("tv", [0, 2], ids=["dimension_split", "matrix_core_rows"])
+def test_denoise_call_staged_frames(ca2, tv):
     """Write pass on a cache with staging slots: the temporal half reads the
     chunk's frames from their ring slots (k_t = v_t = NULL), the spatial half
-    runs in self mode."""
+    runs in self mode; with either temporal form in the fused launch."""
     sh = shape_of(1, 8, 72, 128, 8, 25, 3)
     cache, o = _filled(ca2, sh, 901, [1, 8, 8], staged=True)
     n, C = 8, sh["H"] * sh["d"]
@@ -221,7 +222,11 @@ def test_denoise_call_staged_frames(ca2):
     dqc, dkc, dvc, dqt = (to_dev(x_, "bf16") for x_ in (qc, kc, vc, qt))
     out_s = empty_like_dev(qc.shape, "bf16")
     out_t = empty_like_dev(qc.shape, "bf16")
-    fused = cache.ca2_denoise_attn(dqc, dkc, dvc, out_s, dqt, None, None, out_t, mode=1)
+    ca2.ca2_set_temporal_variant(tv)
+    try:
+        fused = cache.ca2_denoise_attn(dqc, dkc, dvc, out_s, dqt, None, None, out_t, mode=1)
+    finally:
+        ca2.ca2_set_temporal_variant(0)
     torch.cuda.synchronize()
     assert fused
     check_close(to_host(out_s), o.spatial_out(qc, kc, vc, "self"), "bf16", "staged: spatial self")
